@@ -1,0 +1,168 @@
+/*
+ * mlra.h - C ABI of libmlra.so: single-token decode attention over a compressed
+ * latent KV cache, in its Multi-Head Low-Rank Attention form (MLRA-4; also
+ * MLRA-2) and in the absorbed Multi-Head Latent Attention form (MLA), for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (page "Multi-Head Low-Rank Attention", ai.info summary of
+ * arXiv 2603.02188; "Key Contributions" #2 and #3, "Main Findings" bullet 4,
+ * "Methodology in Plain English" paragraphs 1-2): decoding is absorbed-form,
+ * MQA-style attention of h query heads over NB latent heads per cached token.
+ * For sequence b with L = seqlens[b] cached tokens and query head i:
+ *
+ *   u_t      = <q_rope[b,i,:], rope[t,:]>                    (shared by every latent head)
+ *   s_{j,t}  = sm_scale * (<q_nope[b,i,j,:], latent[t,j,:]> + u_t)
+ *   obar_j   = sum_t softmax_t(s_j) * latent[t,j,:]           (one softmax per latent head j)
+ *   out[b,i] = out_scale * sum_j obar_j @ W_UV[j,i]           (W_UV[j,i] is d_latent x d_v)
+ *
+ * q_nope is the query already absorbed into latent coordinates (no per-head
+ * NoPE key or value is ever formed). MLRA-4: NB = 4, d_latent = 128,
+ * out_scale = 1/2. MLRA-2: NB = 2, d_latent = 256, out_scale = 1/sqrt(2).
+ * MLA: NB = 1, d_latent = 512, out_scale = 1. Every form caches
+ * NB*d_latent + d_rope = 512 + 64 elements per token.
+ *
+ * Threading and streams: every call that takes a stream only enqueues work
+ * on that HIP stream (hipStream_t passed as void*, NULL = the null stream) and
+ * returns without synchronising. Device-side faults surface at the caller's
+ * next synchronisation. Calls are thread-safe; error text is thread-local.
+ *
+ * Ownership: every array argument is a device pointer owned by the caller,
+ * except `p` (host). No entry point allocates or frees memory; scratch
+ * memory is the caller's `workspace`.
+ *
+ * Errors: 0 on success, a negative MLRA_ERR_* code otherwise, with a message
+ * in mlra_last_error(). Contract on device data, not checked: 0 <= seqlens[b]
+ * <= max_seqlen, and every block-table entry a sequence uses names a valid
+ * pool page. seqlens[b] == 0 gives out[b] = 0.
+ */
+#ifndef MLRA_H_
+#define MLRA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLRA_ABI_VERSION 1
+
+/* Storage type of q_nope, q_rope, latent_cache and rope_cache.
+ * W_UV and out are always fp32; accumulation is always fp32. */
+enum { MLRA_BF16 = 0, MLRA_F32 = 1 };
+
+enum {
+  MLRA_OK = 0,
+  MLRA_ERR_NULL = -1,        /* a required pointer is NULL */
+  MLRA_ERR_SHAPE = -2,       /* a size or stride is out of range */
+  MLRA_ERR_UNSUPPORTED = -3, /* NB / d_latent / d_rope / d_v / dtype / heads combination not built */
+  MLRA_ERR_ALIGN = -4,       /* a base pointer or row stride is not 16-byte aligned */
+  MLRA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than mlra_decode_workspace_size */
+  MLRA_ERR_HIP = -6          /* the HIP runtime refused a query or a launch */
+};
+
+/* Tokens per tile of the split-KV decode; pages must hold a multiple of it. */
+#define MLRA_TILE_TOKENS 32
+/* Largest number of query heads (two blocks of 32 heads per workgroup). */
+#define MLRA_MAX_HEADS 64
+
+typedef struct mlra_decode_params {
+  int32_t batch;             /* B >= 0 sequences, one new token each */
+  int32_t num_heads;         /* h, 1..MLRA_MAX_HEADS */
+  int32_t num_branches;      /* NB: 4 (MLRA-4), 2 (MLRA-2) or 1 (absorbed MLA) */
+  int32_t d_latent;          /* channels per latent head; must equal 512 / NB */
+  int32_t d_rope;            /* RoPE key channels; must be 64 */
+  int32_t d_v;               /* output channels per head; must be 128 */
+  int32_t dtype;             /* MLRA_BF16 or MLRA_F32 */
+  int32_t page_size;         /* 0: contiguous cache, block_table must be NULL; > 0: paged cache,
+                                block_table required, tokens per page, a multiple of 32 */
+  int32_t max_seqlen;        /* >= every seqlens[b]; contiguous cache: rows reserved per sequence */
+  int32_t max_pages_per_seq; /* paged cache: row stride of block_table (>= ceil(max_seqlen/page_size)) */
+  int32_t num_splits;        /* decode workgroups; 0 = one per resident slot on the device */
+  int32_t reserved;          /* must be 0 */
+  int64_t q_stride_b, q_stride_h;   /* q_nope strides in elements; the NB*d_latent row is contiguous */
+  int64_t qr_stride_b, qr_stride_h; /* q_rope strides in elements; the d_rope row is contiguous */
+  int64_t lat_stride_tok;    /* elements between consecutive cache rows of latent_cache */
+  int64_t rope_stride_tok;   /* elements between consecutive cache rows of rope_cache */
+  float sm_scale;            /* softmax scale (> 0) applied to the full logit, e.g. 1/sqrt(192) */
+  float out_scale;           /* rescale of the branch sum: 1/sqrt(NB) in the MLRA paper's calibration */
+} mlra_decode_params;
+
+/* ABI version of the loaded library (MLRA_ABI_VERSION it was built with). */
+int mlra_abi_version(void);
+
+/* Message for the last non-zero return on the calling thread ("" if none). */
+const char* mlra_last_error(void);
+
+/* Host-only validation of `p` (no HIP call, no device). Returns 0 or a negative code. */
+int mlra_check_params(const mlra_decode_params* p);
+
+/* Decode workgroups a call with `p` launches: p->num_splits if positive, else
+ * (compute units of the current device) x (resident workgroups per unit).
+ * The second case queries the current HIP device. Returns 0 or a negative code. */
+int mlra_decode_num_splits(const mlra_decode_params* p, int32_t* num_splits);
+
+/* Bytes of workspace mlra_decode needs for `p` (uses mlra_decode_num_splits). */
+int mlra_decode_workspace_size(const mlra_decode_params* p, size_t* bytes);
+
+/*
+ * Full decode step: split-KV attention (plan, tile stream, per-latent-head
+ * online softmax, partials) followed by the combine with the fused W_UV
+ * up-projection and branch sum. Two kernel launches on `stream`.
+ *
+ *   q_nope        [B][h] rows of NB*d_latent elements (strides q_stride_b/h); dtype
+ *   q_rope        [B][h] rows of d_rope elements (strides qr_stride_b/h); dtype
+ *   latent_cache  rows of NB*d_latent elements, lat_stride_tok apart; dtype.
+ *                 Contiguous (block_table == NULL): token t of sequence b is row b*max_seqlen + t.
+ *                 Paged: row block_table[b*max_pages_per_seq + t/page_size]*page_size + t%page_size.
+ *   rope_cache    rows of d_rope elements, rope_stride_tok apart, same row numbering; dtype
+ *   block_table   int32 [B][max_pages_per_seq] or NULL
+ *   seqlens       int32 [B] tokens cached per sequence, the new token included
+ *   W_UV          fp32 [NB][h][d_latent][d_v], contiguous (row = latent channel)
+ *   out           fp32 [B][h][d_v], contiguous; fully written
+ *   workspace     device scratch of at least mlra_decode_workspace_size bytes, 256-byte aligned;
+ *                 no contents need to survive between calls
+ * Base pointers of q_nope, q_rope, latent_cache, rope_cache and every row stride
+ * must be 16-byte aligned. Overlapping calls on one workspace race.
+ */
+int mlra_decode(const void* q_nope, const void* q_rope, const void* latent_cache, const void* rope_cache,
+                const int32_t* block_table, const int32_t* seqlens, const float* W_UV, float* out,
+                const mlra_decode_params* p, void* workspace, size_t workspace_bytes, void* stream);
+
+/* First half of mlra_decode alone: the split-KV attention kernel, which leaves
+ * per-split partials (unnormalised output, running max and sum per latent head
+ * and query head) in `workspace`. Same arguments and rules as mlra_decode. */
+int mlra_decode_splitkv(const void* q_nope, const void* q_rope, const void* latent_cache, const void* rope_cache,
+                        const int32_t* block_table, const int32_t* seqlens, const mlra_decode_params* p,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Second half of mlra_decode alone: log-sum-exp merge of the partials that
+ * mlra_decode_splitkv left in `workspace` (same p, same seqlens), then
+ * out[b,i] = out_scale * sum_j obar_j @ W_UV[j,i]. */
+int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, float* out, const mlra_decode_params* p,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The split plan the two kernels follow, written out for inspection. Every
+ * sequence is cut into tiles of MLRA_TILE_TOKENS tokens; the T tiles of all
+ * sequences, in order, are cut into G = min(num_splits, T) contiguous ranges
+ * whose sizes differ by at most one tile; split g writes one partial per
+ * sequence its range touches. Output `plan` (device int32) receives, for split
+ * g < G, rows plan[(g*max_segments + k)*3 + {0,1,2}] = {sequence, first tile,
+ * end tile} (tile numbers local to the sequence), unused rows {-1,-1,-1}; and
+ * plan[num_splits*max_segments*3] = T, plan[.. + 1] = G.
+ * Size of `plan`: num_splits*max_segments*3 + 2 int32. Returns 0 or a negative code.
+ */
+int mlra_decode_plan(const int32_t* seqlens, int32_t batch, int32_t num_splits, int32_t max_segments,
+                     int32_t* plan, void* stream);
+
+/* Plain device copy of `bytes` bytes (16-byte aligned pointers, bytes a multiple
+ * of 16): the achievable-bandwidth reference and the calibration kernel for the
+ * HBM byte counters. */
+int mlra_copy_bandwidth_probe(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* MLRA_H_ */

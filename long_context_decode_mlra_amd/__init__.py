@@ -1,0 +1,154 @@
+"""MLRA-4 / absorbed-MLA single-token decode attention for MI355X (gfx950).
+
+Thin Python binding over libmlra.so (C ABI in include/mlra.h): argument
+marshalling only. Every step of the decode runs in the library's HIP kernels;
+PyTorch supplies device memory and the current stream. There is no fallback:
+if libmlra.so is missing or no GPU is present, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import (MLRA_BF16, MLRA_F32, MLRA_MAX_HEADS, MLRA_TILE_TOKENS, DecodeParams, MlraError, check, lib)
+
+__all__ = ["decode", "decode_splitkv", "decode_combine", "make_params", "Decoder", "workspace_size", "num_splits",
+           "check_params", "plan", "copy_bandwidth_probe", "MlraError", "DecodeParams", "MLRA_BF16", "MLRA_F32",
+           "MLRA_TILE_TOKENS", "MLRA_MAX_HEADS", "lib"]
+
+_DTYPES = {torch.bfloat16: MLRA_BF16, torch.float32: MLRA_F32}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_params(q_nope: torch.Tensor, q_rope: torch.Tensor, latent_cache: torch.Tensor, rope_cache: torch.Tensor,
+                *, sm_scale: float, out_scale: float, max_seqlen: int, page_size: int = 0,
+                max_pages_per_seq: int = 0, num_splits: int = 0) -> DecodeParams:
+    """Fill the C parameter block from tensor shapes and strides.
+
+    q_nope [B, h, NB, DL], q_rope [B, h, DR], latent_cache [rows, NB, DL], rope_cache [rows, DR]:
+    the innermost row of each must be contiguous (views into joint tensors are fine).
+    """
+    B, h, NB, DL = q_nope.shape
+    if q_nope.stride(3) != 1 or q_nope.stride(2) != DL:
+        raise ValueError("q_nope rows [NB, DL] must be contiguous")
+    if q_rope.stride(2) != 1 or latent_cache.stride(2) != 1 or latent_cache.stride(1) != DL \
+            or rope_cache.stride(1) != 1:
+        raise ValueError("q_rope, latent_cache and rope_cache rows must be contiguous")
+    if q_nope.dtype not in _DTYPES or any(t.dtype != q_nope.dtype for t in (q_rope, latent_cache, rope_cache)):
+        raise ValueError("q_nope, q_rope, latent_cache, rope_cache must share one dtype (bfloat16 or float32)")
+    p = DecodeParams()
+    p.batch, p.num_heads, p.num_branches, p.d_latent = B, h, NB, DL
+    p.d_rope, p.d_v = q_rope.shape[2], 128
+    p.dtype = _DTYPES[q_nope.dtype]
+    p.page_size, p.max_seqlen, p.max_pages_per_seq, p.num_splits, p.reserved = \
+        page_size, max_seqlen, max_pages_per_seq, num_splits, 0
+    p.q_stride_b, p.q_stride_h = q_nope.stride(0), q_nope.stride(1)
+    p.qr_stride_b, p.qr_stride_h = q_rope.stride(0), q_rope.stride(1)
+    p.lat_stride_tok, p.rope_stride_tok = latent_cache.stride(0), rope_cache.stride(0)
+    p.sm_scale, p.out_scale = sm_scale, out_scale
+    return p
+
+
+def check_params(p: DecodeParams) -> None:
+    check(lib().mlra_check_params(ctypes.byref(p)))
+
+
+def num_splits(p: DecodeParams) -> int:
+    n = ctypes.c_int32(0)
+    check(lib().mlra_decode_num_splits(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def workspace_size(p: DecodeParams) -> int:
+    n = ctypes.c_size_t(0)
+    check(lib().mlra_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+class Decoder:
+    """One decode configuration with its workspace, for repeated calls on the same shapes."""
+
+    def __init__(self, q_nope, q_rope, latent_cache, rope_cache, *, seqlens, W_UV, sm_scale, out_scale,
+                 max_seqlen, block_table=None, page_size=0, num_splits=0, out=None):
+        maxp = 0 if block_table is None else block_table.shape[1]
+        self.p = make_params(q_nope, q_rope, latent_cache, rope_cache, sm_scale=sm_scale, out_scale=out_scale,
+                             max_seqlen=max_seqlen, page_size=page_size, max_pages_per_seq=maxp,
+                             num_splits=num_splits)
+        for t, name in ((seqlens, "seqlens"), (block_table, "block_table")):
+            if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+                raise ValueError(f"{name} must be a contiguous int32 tensor")
+        if W_UV.dtype != torch.float32 or not W_UV.is_contiguous():
+            raise ValueError("W_UV must be a contiguous float32 tensor [NB, h, DL, DV]")
+        dev = q_nope.device
+        self.tensors = (q_nope, q_rope, latent_cache, rope_cache, block_table, seqlens, W_UV)
+        self.out = out if out is not None else torch.empty(self.p.batch, self.p.num_heads, 128,
+                                                           dtype=torch.float32, device=dev)
+        self.ws_bytes = workspace_size(self.p)
+        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.splits = num_splits if num_splits > 0 else self.num_splits()
+
+    def num_splits(self) -> int:
+        return num_splits(self.p)
+
+    def __call__(self, stream=None) -> torch.Tensor:
+        qn, qr, lat, rp, bt, sl, W = self.tensors
+        check(lib().mlra_decode(_ptr(qn), _ptr(qr), _ptr(lat), _ptr(rp), _ptr(bt), _ptr(sl), _ptr(W),
+                                _ptr(self.out), ctypes.byref(self.p), _ptr(self.workspace), self.ws_bytes,
+                                _stream(stream)))
+        return self.out
+
+    def splitkv(self, stream=None) -> None:
+        qn, qr, lat, rp, bt, sl, _ = self.tensors
+        check(lib().mlra_decode_splitkv(_ptr(qn), _ptr(qr), _ptr(lat), _ptr(rp), _ptr(bt), _ptr(sl),
+                                        ctypes.byref(self.p), _ptr(self.workspace), self.ws_bytes, _stream(stream)))
+
+    def combine(self, stream=None) -> torch.Tensor:
+        sl, W = self.tensors[5], self.tensors[6]
+        check(lib().mlra_decode_combine(_ptr(sl), _ptr(W), _ptr(self.out), ctypes.byref(self.p),
+                                        _ptr(self.workspace), self.ws_bytes, _stream(stream)))
+        return self.out
+
+
+def decode(q_nope, q_rope, latent_cache, rope_cache, seqlens, W_UV, *, sm_scale: float, out_scale: float,
+           max_seqlen: int, block_table=None, page_size: int = 0, num_splits: int = 0, stream=None) -> torch.Tensor:
+    """out[b, i] = out_scale * sum_j softmax-attention of head i over latent head j, up-projected by W_UV[j, i]."""
+    return Decoder(q_nope, q_rope, latent_cache, rope_cache, seqlens=seqlens, W_UV=W_UV, sm_scale=sm_scale,
+                   out_scale=out_scale, max_seqlen=max_seqlen, block_table=block_table, page_size=page_size,
+                   num_splits=num_splits)(stream)
+
+
+def decode_splitkv(dec: Decoder, stream=None) -> None:
+    dec.splitkv(stream)
+
+
+def decode_combine(dec: Decoder, stream=None) -> torch.Tensor:
+    return dec.combine(stream)
+
+
+def plan(seqlens: torch.Tensor, num_splits: int, max_segments: int, stream=None):
+    """The split plan the kernels follow: (segments [G_req, max_segments, 3] int32, total tiles, active splits)."""
+    B = seqlens.numel()
+    buf = torch.empty(num_splits * max_segments * 3 + 2, dtype=torch.int32, device=seqlens.device)
+    check(lib().mlra_decode_plan(_ptr(seqlens), B, num_splits, max_segments, _ptr(buf), _stream(stream)))
+    host = buf.cpu()
+    segs = host[:-2].view(num_splits, max_segments, 3)
+    return segs, int(host[-2]), int(host[-1])
+
+
+def copy_bandwidth_probe(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst smaller than src")
+    check(lib().mlra_copy_bandwidth_probe(_ptr(src), _ptr(dst), nbytes, _stream(stream)))

@@ -1,0 +1,912 @@
+// Split-KV decode attention for MLRA (NB latent heads per token) and absorbed MLA
+// on gfx950, behind the C ABI of include/mlra.h.
+//
+// The computation (page "Multi-Head Low-Rank Attention", ai.info summary of
+// arXiv 2603.02188): absorbed decode is MQA-style attention of every query head
+// over the latent cache followed by the value up-projection ("Main Findings"
+// bullet 4). MLRA runs that attention once per latent head with its own softmax
+// and sums the per-head up-projected outputs, scaled for the branch count
+// ("Key Contributions" #2, #3). Each branch's logit adds the shared RoPE logit
+// (per-branch logit space 128 + 64, "Key Contributions" #2).
+//
+// Kernels
+//   decode_kernel   one workgroup per split; streams 32-token tiles of the cache
+//                   (latent rows + RoPE rows) HBM -> registers -> LDS, computes
+//                   S^T = K Q^T and O^T += V^T P^T on bf16 (or fp32) MFMA for all
+//                   query heads of the split's sequence, keeps an fp32 online
+//                   softmax per (latent head, query head), and writes one partial
+//                   (unnormalised O, running max, running sum) per sequence it touches.
+//   combine_kernel  log-sum-exp merge of a sequence's partials, then the fused
+//                   W_UV up-projection, branch sum and output scale.
+// Splitting is balanced over the flattened tiles of all sequences (the plan).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "mlra_internal.h"
+
+namespace mlra {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+// A running max is only raised once the tile max exceeds it by this many
+// log2 units, so exp2 arguments stay <= 8 and unneeded rescales are skipped.
+// The final result is exact either way: numerator and denominator share the max.
+constexpr float kRescaleSlack = 8.0f;
+
+// ------------------------------------------------------------------ split plan
+// All sequences are cut into tiles of kTile tokens; the T tiles, taken in
+// sequence order, are cut into G = min(G_req, T) contiguous ranges of
+// floor/ceil(T/G) tiles. Range g = [g*T/G, (g+1)*T/G). Split g writes its
+// partial for sequence b into slot g + b: ranges are ordered, so the sequences
+// split g touches are >= those of any earlier split, which makes g + b unique.
+
+__device__ __forceinline__ int64_t tiles_of(int L) { return (int64_t(L) + kTile - 1) / kTile; }
+
+struct Plan {
+  int64_t T;
+  int G;
+};
+
+__device__ __forceinline__ int64_t wave_sum(int64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Every lane of the calling wave gets the same plan.
+__device__ Plan make_plan(const int32_t* __restrict__ seqlens, int B, int G_req) {
+  const int lane = threadIdx.x & 63;
+  int64_t s = 0;
+  for (int b = lane; b < B; b += 64) s += tiles_of(seqlens[b]);
+  Plan p;
+  p.T = wave_sum(s);
+  p.G = int(p.T < G_req ? p.T : G_req);
+  return p;
+}
+
+__device__ __forceinline__ int64_t split_begin(int64_t g, const Plan& p) { return g * p.T / p.G; }
+
+// Largest split g whose range starts at or before tile x (x < T): the split holding tile x.
+__device__ __forceinline__ int64_t split_of_tile(int64_t x, const Plan& p) {
+  return ((x + 1) * p.G - 1) / p.T;
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int64_t wave_inclusive_scan(int64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
+  }
+  return v;
+}
+
+// The sequence b holding global tile x (< T) and its first global tile P_b.
+__device__ void find_sequence(const int32_t* __restrict__ seqlens, int B, int64_t x, int& b_out,
+                              int64_t& P_out) {
+  const int lane = threadIdx.x & 63;
+  int64_t carry = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    const int64_t t = b < B ? tiles_of(seqlens[b]) : 0;
+    const int64_t incl = wave_inclusive_scan(t);
+    const int64_t excl = carry + incl - t;
+    const unsigned long long hit = __ballot(b < B && t > 0 && excl <= x && x < excl + t);
+    if (hit) {
+      const int src = __ffsll(hit) - 1;
+      b_out = base + src;
+      P_out = __shfl(excl, src, 64);
+      return;
+    }
+    carry += __shfl(incl, 63, 64);
+  }
+  b_out = B;
+  P_out = carry;
+}
+
+struct SegmentWalk {
+  int b;       // current sequence
+  int64_t Pb;  // its first global tile
+  int64_t cur; // next global tile to hand out
+  int64_t end; // end of this split's range
+};
+
+__device__ SegmentWalk begin_walk(const int32_t* __restrict__ seqlens, int B, int64_t g, const Plan& p) {
+  SegmentWalk w;
+  w.cur = split_begin(g, p);
+  w.end = split_begin(g + 1, p);
+  find_sequence(seqlens, B, w.cur, w.b, w.Pb);
+  return w;
+}
+
+// Next (sequence, first tile, end tile) of the split, tiles local to the sequence.
+__device__ bool next_segment(const int32_t* __restrict__ seqlens, int B, SegmentWalk& w, int& b, int& ta,
+                             int& te) {
+  while (w.cur < w.end && w.b < B) {
+    const int64_t n = tiles_of(seqlens[w.b]);
+    const int64_t seg_end = w.end < w.Pb + n ? w.end : w.Pb + n;
+    if (n > 0 && w.cur < seg_end) {
+      b = w.b;
+      ta = int(w.cur - w.Pb);
+      te = int(seg_end - w.Pb);
+      w.cur = seg_end;
+      if (seg_end == w.Pb + n) {
+        w.Pb += n;
+        ++w.b;
+      }
+      return true;
+    }
+    w.Pb += n;
+    ++w.b;
+  }
+  return false;
+}
+
+// ------------------------------------------------------------------ decode kernel
+
+// Workgroup barrier that orders LDS only. __syncthreads() also waits for every
+// outstanding global load of the wave (its release fence drains vmcnt), which
+// would drain the prefetch of the next tile; here only LDS traffic is drained.
+// The asm statement is also a compiler memory barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+struct DecodeArgs {
+  const unsigned char* q_nope;
+  const unsigned char* q_rope;
+  const unsigned char* latent;
+  const unsigned char* rope;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  float* part_o;
+  float* part_ml;
+  int B, h, G_req, page_size, max_seqlen, max_pages;
+  int64_t q_sb, q_sh, qr_sb, qr_sh;  // bytes
+  int64_t lat_stride, rope_stride;   // bytes
+  float c;                           // sm_scale * log2(e)
+};
+
+// Tile geometry. The LDS copy of a tile keeps the cache row order; within each
+// row the 16-byte chunk c of token t sits at chunk position c ^ (t & 7), so the
+// MFMA operand reads (32 tokens at one chunk, or 8-byte column groups of one
+// token) hit distinct banks.
+template <typename T, int NB, int HB>
+struct Geo {
+  static constexpr int kEsz = int(sizeof(T));
+  static constexpr int kLatRow = kLatentTotal * kEsz;  // bytes of one token's latent row
+  static constexpr int kRopeRow = kDRope * kEsz;       // bytes of one token's RoPE row
+  static constexpr int kLatTile = kTile * kLatRow;
+  static constexpr int kTileBytes = kLatTile + kTile * kRopeRow;
+  static constexpr int kWaves = 4 * HB;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kInst = kTileBytes / 1024;  // 64 lanes x 16 bytes per load
+  static constexpr int kInstPerWave = (kInst + kWaves - 1) / kWaves;
+  static constexpr int kWPB = 4 / NB;  // waves sharing one latent head (each owns 128 channels)
+  static constexpr int kDL = kLatentTotal / NB;
+  static constexpr int kLds = 2 * kTileBytes;
+  // Loads go straight into LDS unless the idle tile buffer is needed for the
+  // logit exchange between the waves that share one latent head.
+  static constexpr bool kDirect = (kWPB == 1);
+  static_assert(kLatTile % 1024 == 0 && kTileBytes % 1024 == 0, "tile must be whole 1 KiB loads");
+  static_assert(kWaves * 4096 <= kTileBytes, "logit exchange must fit the idle tile buffer");
+};
+
+// Per-lane MFMA operands of the query: lane (n, hh) supplies query head 32*hb + n.
+template <typename T, int NB>
+struct QOps;
+
+template <int NB>
+struct QOps<__bf16, NB> {
+  static constexpr int kRopeSteps = NB;  // 16-channel RoPE k-steps per wave: 64 / 16 / (4 / NB)
+  bf16x8 lat[8];
+  bf16x8 rope[kRopeSteps];
+};
+
+template <int NB>
+struct QOps<float, NB> {
+  static constexpr int kRopeGroups = 2 * NB;  // 8-channel RoPE groups per wave: 64 / 8 / (4 / NB)
+  floatx4 lat[16];
+  floatx4 rope[kRopeGroups];
+};
+
+template <typename T, int NB, int HB>
+__device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int head, bool head_ok, int wq, int sub, int hh,
+                                       QOps<T, NB>& q) {
+  using G = Geo<T, NB, HB>;
+  const unsigned char* qn = a.q_nope + int64_t(b) * a.q_sb + int64_t(head) * a.q_sh + 128 * wq * G::kEsz;
+  const unsigned char* qr = a.q_rope + int64_t(b) * a.qr_sb + int64_t(head) * a.qr_sh;
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      q.lat[ks] = head_ok ? *reinterpret_cast<const bf16x8*>(qn + (16 * ks + 8 * hh) * 2) : bf16x8{};
+#pragma unroll
+    for (int rs = 0; rs < QOps<T, NB>::kRopeSteps; ++rs) {
+      const int ks = sub * QOps<T, NB>::kRopeSteps + rs;
+      q.rope[rs] = head_ok ? *reinterpret_cast<const bf16x8*>(qr + (16 * ks + 8 * hh) * 2) : bf16x8{};
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < 16; ++g)
+      q.lat[g] = head_ok ? *reinterpret_cast<const floatx4*>(qn + (8 * g + 4 * hh) * 4) : floatx4{};
+#pragma unroll
+    for (int rg = 0; rg < QOps<T, NB>::kRopeGroups; ++rg) {
+      const int g = sub * QOps<T, NB>::kRopeGroups + rg;
+      q.rope[rg] = head_ok ? *reinterpret_cast<const floatx4*>(qr + (8 * g + 4 * hh) * 4) : floatx4{};
+    }
+  }
+}
+
+// Source of 16-byte load `inst` (0 .. kInst-1) of a tile for lane `lane`: the
+// load fills LDS bytes [inst*1024 + 16*lane, +16) of the tile. Tokens past the
+// end of the sequence re-read its last token (valid data; their logits are masked).
+struct TileRows {
+  const unsigned char* lat;  // latent row of the tile's first token
+  const unsigned char* rope; // RoPE row of the tile's first token
+  int last;                  // index of the tile's last valid token
+};
+
+__device__ __forceinline__ TileRows tile_rows(const DecodeArgs& a, int b, int L, int tile) {
+  const int tok0 = tile * kTile;
+  int64_t row0;
+  if (a.block_table) {
+    // Pages hold a multiple of kTile tokens, so a tile never straddles two pages.
+    const int page = a.block_table[int64_t(b) * a.max_pages + tok0 / a.page_size];
+    row0 = int64_t(page) * a.page_size + tok0 % a.page_size;
+  } else {
+    row0 = int64_t(b) * a.max_seqlen + tok0;
+  }
+  TileRows r;
+  r.lat = a.latent + row0 * a.lat_stride;
+  r.rope = a.rope + row0 * a.rope_stride;
+  r.last = min(kTile, L - tok0) - 1;
+  return r;
+}
+
+template <typename T, int NB, int HB>
+__device__ __forceinline__ const unsigned char* load_src(const DecodeArgs& a, const TileRows& tr, int inst,
+                                                         int lane) {
+  using G = Geo<T, NB, HB>;
+  const int off = inst * 1024 + lane * 16;
+  // Offsets inside one tile fit 32 bits: 32 rows times a stride below 2^25 bytes.
+  if (off < G::kLatTile) {
+    const int t = off / G::kLatRow;
+    const int c = ((off % G::kLatRow) >> 4) ^ (t & 7);
+    return tr.lat + (min(t, tr.last) * int(a.lat_stride) + c * 16);
+  }
+  const int o2 = off - G::kLatTile;
+  const int t = o2 / G::kRopeRow;
+  const int c = ((o2 % G::kRopeRow) >> 4) ^ (t & 7);
+  return tr.rope + (min(t, tr.last) * int(a.rope_stride) + c * 16);
+}
+
+// Register-staged loader: this wave's loads of one tile into registers.
+template <typename T, int NB, int HB>
+__device__ __forceinline__ void issue_tile_loads(const DecodeArgs& a, int b, int L, int tile, int wave, int lane,
+                                                 u32x4 (&stg)[Geo<T, NB, HB>::kInstPerWave]) {
+  using G = Geo<T, NB, HB>;
+  const TileRows tr = tile_rows(a, b, L, tile);
+#pragma unroll
+  for (int i = 0; i < G::kInstPerWave; ++i) {
+    const int inst = wave + i * G::kWaves;
+    if (inst < G::kInst) stg[i] = *reinterpret_cast<const u32x4*>(load_src<T, NB, HB>(a, tr, inst, lane));
+  }
+}
+
+// Direct loader: this wave's loads of one tile go straight from HBM into LDS
+// (each load writes 64 lanes x 16 bytes contiguously at the given LDS address).
+// Completion is tracked by the wave's vector-memory counter.
+template <typename T, int NB, int HB>
+__device__ __forceinline__ void issue_tile_dma(const DecodeArgs& a, int b, int L, int tile, int wave, int lane,
+                                               unsigned char* buf) {
+  using G = Geo<T, NB, HB>;
+  const TileRows tr = tile_rows(a, b, L, tile);
+#pragma unroll
+  for (int i = 0; i < G::kInstPerWave; ++i) {
+    const int inst = wave + i * G::kWaves;
+    if (inst < G::kInst) {
+      const unsigned char* src = load_src<T, NB, HB>(a, tr, inst, lane);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(buf + inst * 1024), 16, 0, 0);
+    }
+  }
+}
+
+template <typename T, int NB, int HB>
+__device__ __forceinline__ void store_tile(unsigned char* buf, int wave, int lane,
+                                           const u32x4 (&stg)[Geo<T, NB, HB>::kInstPerWave]) {
+  using G = Geo<T, NB, HB>;
+#pragma unroll
+  for (int i = 0; i < G::kInstPerWave; ++i) {
+    const int inst = wave + i * G::kWaves;
+    if (inst < G::kInst) *reinterpret_cast<u32x4*>(buf + inst * 1024 + lane * 16) = stg[i];
+  }
+}
+
+// S^T[token][head] partial over this wave's 128 latent channels and its share of the RoPE channels.
+template <typename T, int NB, int HB>
+__device__ __forceinline__ floatx16 tile_logits(const unsigned char* buf, int wq, int n, int hh,
+                                                const QOps<T, NB>& q) {
+  using G = Geo<T, NB, HB>;
+  floatx16 s = {};
+  const unsigned char* row = buf + n * G::kLatRow;
+  const unsigned char* rrow = buf + G::kLatTile + n * G::kRopeRow;
+  const int sw = n & 7;
+  const int sub = wq % G::kWPB;
+  if constexpr (sizeof(T) == 2) {
+    // Chunk 16*wq + 2*ks + hh of row n sits at ((2*(ks&3) + hh) ^ sw) + 8*(ks>>2) + 16*wq:
+    // four lane-dependent bases, the rest are immediate offsets.
+    const unsigned char* base = row + (wq << 8);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const bf16x8 k = *reinterpret_cast<const bf16x8*>(base + (((2 * (ks & 3) + hh) ^ sw) << 4) + ((ks >> 2) << 7));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, q.lat[ks], s, 0, 0, 0);
+    }
+#pragma unroll
+    for (int rs = 0; rs < QOps<T, NB>::kRopeSteps; ++rs) {
+      const int ks = sub * QOps<T, NB>::kRopeSteps + rs;
+      const bf16x8 k = *reinterpret_cast<const bf16x8*>(rrow + (((2 * ks + hh) ^ sw) << 4));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, q.rope[rs], s, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const floatx4 k = *reinterpret_cast<const floatx4*>(row + (((32 * wq + 2 * g + hh) ^ sw) << 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(k[e], q.lat[g][e], s, 0, 0, 0);
+    }
+#pragma unroll
+    for (int rg = 0; rg < QOps<T, NB>::kRopeGroups; ++rg) {
+      const int g = sub * QOps<T, NB>::kRopeGroups + rg;
+      const floatx4 k = *reinterpret_cast<const floatx4*>(rrow + (((2 * g + hh) ^ sw) << 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(k[e], q.rope[rg][e], s, 0, 0, 0);
+    }
+  }
+  return s;
+}
+
+// O^T[channel][head] += V^T P^T over the tile. Register r of lane half hh holds
+// the weight of token tau = 8*(r/4) + 4*hh + r%4; output row m of M-block mb is
+// latent channel 4*m + mb of this wave's 128 channels.
+template <typename T, int NB, int HB>
+__device__ __forceinline__ void tile_pv(const unsigned char* buf, int wq, int n, int hh, const floatx16& p,
+                                        floatx16 (&O)[4]) {
+  using G = Geo<T, NB, HB>;
+  if constexpr (sizeof(T) == 2) {
+    // Token tau = 16*ks + 8*(e>>2) + 4*hh + (e&3) has tau & 7 = 4*hh + (e&3): four
+    // lane-dependent bases (one per e&3); the token's row offset is an immediate.
+    const unsigned char* vb[4];
+#pragma unroll
+    for (int e3 = 0; e3 < 4; ++e3)
+      vb[e3] = buf + (4 * hh + e3) * G::kLatRow + (((16 * wq + (n >> 1)) ^ (4 * hh + e3)) << 4) + ((n & 1) << 3);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const floatx2 f = {p[8 * ks + e], p[8 * ks + e + 1]};
+        const bf16x2 v = __builtin_convertvector(f, bf16x2);
+        pb[e] = v[0];
+        pb[e + 1] = v[1];
+      }
+      u32x2 d[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        d[e] = *reinterpret_cast<const u32x2*>(vb[e & 3] + (16 * ks + 8 * (e >> 2)) * G::kLatRow);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const uint32_t sel = (mb & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 av;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const uint32_t lo = (mb < 2) ? d[2 * pp][0] : d[2 * pp][1];
+          const uint32_t hi = (mb < 2) ? d[2 * pp + 1][0] : d[2 * pp + 1][1];
+          av[pp] = __builtin_amdgcn_perm(hi, lo, sel);
+        }
+        O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb, O[mb], 0, 0, 0);
+      }
+    }
+  } else {
+    // Token tau = 8*(r>>2) + 4*hh + (r&3): tau & 7 = 4*hh + (r&3).
+    const unsigned char* vb[4];
+#pragma unroll
+    for (int r3 = 0; r3 < 4; ++r3)
+      vb[r3] = buf + (4 * hh + r3) * G::kLatRow + (((32 * wq + n) ^ (4 * hh + r3)) << 4);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const floatx4 v = *reinterpret_cast<const floatx4*>(vb[r & 3] + 8 * (r >> 2) * G::kLatRow);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) O[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v[mb], p[r], O[mb], 0, 0, 0);
+    }
+  }
+}
+
+template <typename T, int NB, int HB>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, 256 * HB), amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, 2)))
+void decode_kernel(DecodeArgs a) {
+  using G = Geo<T, NB, HB>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[G::kLds];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets tile addressing stay scalar
+  const int hb = wave >> 2;       // block of 32 query heads
+  const int wq = wave & 3;        // which 128 of the 512 latent channels this wave owns
+  const int j = wq / G::kWPB;     // latent head (branch)
+  const int sub = wq % G::kWPB;   // part of the branch
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int head = hb * kHeadBlock + n;
+  const bool head_ok = head < a.h;
+
+  const Plan plan = make_plan(a.seqlens, a.B, a.G_req);
+  const int g = blockIdx.x;
+  if (g >= plan.G) return;
+  SegmentWalk walk = begin_walk(a.seqlens, a.B, g, plan);
+
+  int b, ta, te;
+  while (next_segment(a.seqlens, a.B, walk, b, ta, te)) {
+    const int L = a.seqlens[b];
+    QOps<T, NB> q;
+    load_q<T, NB, HB>(a, b, head, head_ok, wq, sub, hh, q);
+    floatx16 O[4] = {};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    // Two LDS tile buffers; tile k+1 is in flight (in registers, or already on its way
+    // into the other buffer) while tile k is computed.
+    [[maybe_unused]] u32x4 stg[G::kDirect ? 1 : G::kInstPerWave];
+    if constexpr (G::kDirect) issue_tile_dma<T, NB, HB>(a, b, L, ta, wave, lane, smem);
+    else issue_tile_loads<T, NB, HB>(a, b, L, ta, wave, lane, stg);
+    for (int k = ta; k < te; ++k) {
+      unsigned char* buf = smem + ((k - ta) & 1) * G::kTileBytes;
+      unsigned char* idle = smem + (((k - ta) & 1) ^ 1) * G::kTileBytes;
+      if constexpr (G::kDirect) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile k has landed
+        lds_barrier();  // every wave's part landed; every wave is done with tile k-1's buffer
+        if (k + 1 < te) issue_tile_dma<T, NB, HB>(a, b, L, k + 1, wave, lane, idle);
+      } else {
+        store_tile<T, NB, HB>(buf, wave, lane, stg);
+        if (k + 1 < te) issue_tile_loads<T, NB, HB>(a, b, L, k + 1, wave, lane, stg);
+        lds_barrier();  // tile k visible to every wave; tile k+1 stays in flight
+      }
+
+      floatx16 s = tile_logits<T, NB, HB>(buf, wq, n, hh, q);
+      if constexpr (G::kWPB > 1) {
+        // Sum the partial logits of the waves that share this latent head, in a fixed order,
+        // so every one of them holds bit-identical logits.
+        floatx4* red = reinterpret_cast<floatx4*>(idle);
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          red[(wave * 4 + qq) * 64 + lane] = floatx4{s[4 * qq], s[4 * qq + 1], s[4 * qq + 2], s[4 * qq + 3]};
+        lds_barrier();
+        floatx16 tot = {};
+#pragma unroll
+        for (int w2 = 0; w2 < G::kWPB; ++w2) {
+          const int src = hb * 4 + j * G::kWPB + w2;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const floatx4 v = red[(src * 4 + qq) * 64 + lane];
+            tot[4 * qq] += v[0];
+            tot[4 * qq + 1] += v[1];
+            tot[4 * qq + 2] += v[2];
+            tot[4 * qq + 3] += v[3];
+          }
+        }
+        lds_barrier();  // exchange area free again before the next tile is stored there
+        s = tot;
+      }
+
+      const int n_valid = L - k * kTile;
+      if (n_valid < kTile) {
+        // Register r of lane half hh holds token 8*(r>>2) + 4*hh + (r&3).
+        const int lim = n_valid - 4 * hh;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) >= lim) s[r] = -INFINITY;
+      }
+
+      // Online softmax in log2 units: x = s * sm_scale * log2(e).
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mt = mx * a.c;
+      const bool raise = mt > m_run + kRescaleSlack;
+      if (__ballot(raise)) {
+        const float mnew = raise ? mt : m_run;
+        const float alpha = (mnew == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
+        l_run *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) O[mb] *= alpha;
+        m_run = mnew;
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -m_run));
+        psum += s[r];
+      }
+      l_run += psum;
+      tile_pv<T, NB, HB>(buf, wq, n, hh, s, O);
+    }
+    lds_barrier();  // both tile buffers free before the next segment
+
+    // Partial of split g for sequence b, slot g + b.
+    const int64_t slot = int64_t(g) + b;
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (head_ok) {
+      float* dst = a.part_o + ((slot * NB + j) * a.h + head) * G::kDL + sub * 128;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<floatx4*>(dst + 32 * gg + 16 * hh + 4 * i) =
+              floatx4{O[0][4 * gg + i], O[1][4 * gg + i], O[2][4 * gg + i], O[3][4 * gg + i]};
+      if (hh == 0 && sub == 0) {
+        float* ml = a.part_ml + ((slot * NB + j) * a.h + head) * 2;
+        ml[0] = m_run;
+        ml[1] = l_tot;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ combine kernel
+
+struct CombineArgs {
+  const int32_t* seqlens;
+  const float* part_o;
+  const float* part_ml;
+  const float* W_UV;
+  float* out;
+  int B, h, G_req;
+  float out_scale;
+};
+
+constexpr int kCombineSeqs = 4;  // sequences per combine workgroup (W_UV rows reused across them)
+
+template <int NB>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  constexpr int DL = kLatentTotal / NB;
+  __shared__ float obar[kCombineSeqs][kLatentTotal];
+  __shared__ long long sP[kCombineSeqs + 1];
+  __shared__ long long sT;
+  __shared__ int sG;
+
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x;  // query head
+  const int b0 = blockIdx.y * kCombineSeqs;
+
+  if (tid < 64) {
+    const Plan plan = make_plan(a.seqlens, a.B, a.G_req);
+    int64_t carry = 0;
+    for (int base = 0; base < a.B; base += 64) {
+      const int b = base + tid;
+      const int64_t t = b < a.B ? tiles_of(a.seqlens[b]) : 0;
+      const int64_t incl = wave_inclusive_scan(t);
+      if (b < a.B && b >= b0 && b < b0 + kCombineSeqs) {
+        sP[b - b0] = carry + incl - t;
+        sP[b - b0 + 1] = carry + incl;
+      }
+      carry += __shfl(incl, 63, 64);
+    }
+    if (tid == 0) {
+      sT = plan.T;
+      sG = plan.G;
+    }
+  }
+  __syncthreads();
+  const Plan plan{sT, sG};
+
+  for (int bl = 0; bl < kCombineSeqs; ++bl) {
+    const int b = b0 + bl;
+    if (b >= a.B) break;
+    const int64_t P0 = sP[bl], P1 = sP[bl + 1];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int kk = tid + 256 * h2;
+      const int j = kk / DL, c = kk % DL;
+      float v = 0.f;
+      if (P1 > P0) {
+        const int64_t gf = split_of_tile(P0, plan), gl = split_of_tile(P1 - 1, plan);
+        float M = -INFINITY;
+        for (int64_t gg = gf; gg <= gl; ++gg) M = fmaxf(M, a.part_ml[(((gg + b) * NB + j) * a.h + i) * 2]);
+        float num = 0.f, den = 0.f;
+        for (int64_t gg = gf; gg <= gl; ++gg) {
+          const int64_t r = ((gg + b) * NB + j) * a.h + i;
+          const float w = __builtin_amdgcn_exp2f(a.part_ml[r * 2] - M);
+          num = fmaf(w, a.part_o[r * DL + c], num);
+          den = fmaf(w, a.part_ml[r * 2 + 1], den);
+        }
+        v = num / den;
+      }
+      obar[bl][kk] = v;
+    }
+  }
+  __syncthreads();
+
+  // out[b, i, d] = out_scale * sum_k obar[b][k] * W_UV[j(k), i, c(k), d], k = j*DL + c.
+  const int d = tid & 127;
+  const int bl0 = tid >> 7;  // this thread covers sequences bl0 and bl0 + 2
+  float acc0 = 0.f, acc1 = 0.f;
+  for (int j = 0; j < NB; ++j) {
+    const float* w = a.W_UV + ((int64_t(j) * a.h + i) * DL) * kDV + d;
+    for (int c = 0; c < DL; ++c) {
+      const float wv = w[int64_t(c) * kDV];
+      acc0 = fmaf(obar[bl0][j * DL + c], wv, acc0);
+      acc1 = fmaf(obar[bl0 + 2][j * DL + c], wv, acc1);
+    }
+  }
+  if (b0 + bl0 < a.B) a.out[(int64_t(b0 + bl0) * a.h + i) * kDV + d] = a.out_scale * acc0;
+  if (b0 + bl0 + 2 < a.B) a.out[(int64_t(b0 + bl0 + 2) * a.h + i) * kDV + d] = a.out_scale * acc1;
+}
+
+// ------------------------------------------------------------------ plan dump and copy probe
+
+__global__ __launch_bounds__(64) void plan_kernel(const int32_t* seqlens, int B, int G_req, int max_seg,
+                                                  int32_t* out) {
+  const int g = blockIdx.x;
+  const int lane = threadIdx.x;
+  int32_t* row = out + int64_t(g) * max_seg * 3;
+  for (int k = lane; k < max_seg * 3; k += 64) row[k] = -1;
+  const Plan plan = make_plan(seqlens, B, G_req);
+  if (g == 0 && lane == 0) {
+    out[int64_t(G_req) * max_seg * 3] = int32_t(plan.T);
+    out[int64_t(G_req) * max_seg * 3 + 1] = plan.G;
+  }
+  if (g >= plan.G) return;
+  SegmentWalk walk = begin_walk(seqlens, B, g, plan);
+  int b, ta, te, k = 0;
+  while (next_segment(seqlens, B, walk, b, ta, te)) {
+    if (lane == 0 && k < max_seg) {
+      row[3 * k] = b;
+      row[3 * k + 1] = ta;
+      row[3 * k + 2] = te;
+    }
+    ++k;
+  }
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                   int64_t n) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+// ------------------------------------------------------------------ host side
+
+using DecodeFn = void (*)(DecodeArgs);
+using CombineFn = void (*)(CombineArgs);
+
+DecodeFn pick_decode(int dtype, int nb, int hb) {
+#define MLRA_PICK(T, NB_)                                                        \
+  if (nb == NB_) return hb == 1 ? decode_kernel<T, NB_, 1> : decode_kernel<T, NB_, 2>;
+  if (dtype == MLRA_BF16) {
+    MLRA_PICK(__bf16, 4)
+    MLRA_PICK(__bf16, 2)
+    MLRA_PICK(__bf16, 1)
+  } else {
+    MLRA_PICK(float, 4)
+    MLRA_PICK(float, 2)
+    MLRA_PICK(float, 1)
+  }
+#undef MLRA_PICK
+  return nullptr;
+}
+
+CombineFn pick_combine(int nb) {
+  switch (nb) {
+    case 4: return combine_kernel<4>;
+    case 2: return combine_kernel<2>;
+    default: return combine_kernel<1>;
+  }
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return set_error(MLRA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Resident decode workgroups per device, cached per (device, kernel).
+int resident_splits(const mlra_decode_params& p, int32_t* out) {
+  static std::mutex mu;
+  static int cache[64][2][3][2];  // device, dtype, log2 NB, HB-1
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  const int hb = head_blocks(p.num_heads);
+  const int nbi = p.num_branches == 4 ? 2 : p.num_branches == 2 ? 1 : 0;
+  if (dev >= 0 && dev < 64) {
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache[dev][p.dtype][nbi][hb - 1] > 0) {
+      *out = cache[dev][p.dtype][nbi][hb - 1];
+      return MLRA_OK;
+    }
+  }
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(pick_decode(p.dtype, p.num_branches, hb)),
+                                                   256 * hb, 0);
+  if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  if (per_cu < 1) per_cu = 1;
+  const int n = cus * per_cu;
+  if (dev >= 0 && dev < 64) {
+    std::lock_guard<std::mutex> lk(mu);
+    cache[dev][p.dtype][nbi][hb - 1] = n;
+  }
+  *out = n;
+  return MLRA_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+int prepare(const mlra_decode_params* p, const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+            int32_t* G, WorkspaceLayout* lay) {
+  int rc = mlra_check_params(p);
+  if (rc) return rc;
+  rc = mlra_decode_num_splits(p, G);
+  if (rc) return rc;
+  *lay = workspace_layout(*p, *G);
+  if (p->batch == 0) return MLRA_OK;
+  if (!seqlens) return set_error(MLRA_ERR_NULL, "seqlens is NULL");
+  if (!workspace) return set_error(MLRA_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return set_error(MLRA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < lay->total)
+    return set_error(MLRA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, lay->total);
+  return MLRA_OK;
+}
+
+}  // namespace
+}  // namespace mlra
+
+using namespace mlra;
+
+extern "C" int mlra_decode_num_splits(const mlra_decode_params* p, int32_t* num_splits) {
+  const int rc = mlra_check_params(p);
+  if (rc) return rc;
+  if (!num_splits) return set_error(MLRA_ERR_NULL, "num_splits output pointer is NULL");
+  if (p->num_splits > 0) {
+    *num_splits = p->num_splits;
+    return MLRA_OK;
+  }
+  return resident_splits(*p, num_splits);
+}
+
+extern "C" int mlra_decode_workspace_size(const mlra_decode_params* p, size_t* bytes) {
+  if (!bytes) return set_error(MLRA_ERR_NULL, "bytes output pointer is NULL");
+  int32_t G = 0;
+  const int rc = mlra_decode_num_splits(p, &G);
+  if (rc) return rc;
+  *bytes = workspace_layout(*p, G).total;
+  return MLRA_OK;
+}
+
+extern "C" int mlra_decode_splitkv(const void* q_nope, const void* q_rope, const void* latent_cache,
+                                   const void* rope_cache, const int32_t* block_table, const int32_t* seqlens,
+                                   const mlra_decode_params* p, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  int32_t G = 0;
+  WorkspaceLayout lay;
+  int rc = prepare(p, seqlens, workspace, workspace_bytes, &G, &lay);
+  if (rc) return rc;
+  if (p->batch == 0) return MLRA_OK;
+  if (!q_nope || !q_rope || !latent_cache || !rope_cache)
+    return set_error(MLRA_ERR_NULL, "q_nope, q_rope, latent_cache and rope_cache must be non-NULL");
+  if ((p->page_size > 0) != (block_table != nullptr))
+    return set_error(MLRA_ERR_NULL, "block_table must be given exactly when page_size > 0");
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(latent_cache) || !aligned16(rope_cache))
+    return set_error(MLRA_ERR_ALIGN, "q_nope, q_rope, latent_cache and rope_cache must be 16-byte aligned");
+
+  const int64_t esz = p->dtype == MLRA_BF16 ? 2 : 4;
+  DecodeArgs a;
+  a.q_nope = static_cast<const unsigned char*>(q_nope);
+  a.q_rope = static_cast<const unsigned char*>(q_rope);
+  a.latent = static_cast<const unsigned char*>(latent_cache);
+  a.rope = static_cast<const unsigned char*>(rope_cache);
+  a.block_table = block_table;
+  a.seqlens = seqlens;
+  a.part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + lay.part_o_off);
+  a.part_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + lay.part_ml_off);
+  a.B = p->batch;
+  a.h = p->num_heads;
+  a.G_req = G;
+  a.page_size = p->page_size > 0 ? p->page_size : 1;
+  a.max_seqlen = p->max_seqlen;
+  a.max_pages = p->max_pages_per_seq;
+  a.q_sb = p->q_stride_b * esz;
+  a.q_sh = p->q_stride_h * esz;
+  a.qr_sb = p->qr_stride_b * esz;
+  a.qr_sh = p->qr_stride_h * esz;
+  a.lat_stride = p->lat_stride_tok * esz;
+  a.rope_stride = p->rope_stride_tok * esz;
+  a.c = p->sm_scale * kLog2e;
+
+  const int hb = head_blocks(p->num_heads);
+  DecodeFn fn = pick_decode(p->dtype, p->num_branches, hb);
+  if (!fn) return set_error(MLRA_ERR_UNSUPPORTED, "no decode kernel for this configuration");
+  hipLaunchKernelGGL(fn, dim3(G), dim3(256 * hb), 0, static_cast<hipStream_t>(stream), a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
+  return MLRA_OK;
+}
+
+extern "C" int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, float* out,
+                                   const mlra_decode_params* p, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  int32_t G = 0;
+  WorkspaceLayout lay;
+  int rc = prepare(p, seqlens, workspace, workspace_bytes, &G, &lay);
+  if (rc) return rc;
+  if (p->batch == 0) return MLRA_OK;
+  if (!W_UV || !out) return set_error(MLRA_ERR_NULL, "W_UV and out must be non-NULL");
+  CombineArgs a;
+  a.seqlens = seqlens;
+  a.part_o = reinterpret_cast<const float*>(static_cast<unsigned char*>(workspace) + lay.part_o_off);
+  a.part_ml = reinterpret_cast<const float*>(static_cast<unsigned char*>(workspace) + lay.part_ml_off);
+  a.W_UV = W_UV;
+  a.out = out;
+  a.B = p->batch;
+  a.h = p->num_heads;
+  a.G_req = G;
+  a.out_scale = p->out_scale;
+  const dim3 grid(p->num_heads, (p->batch + kCombineSeqs - 1) / kCombineSeqs);
+  hipLaunchKernelGGL(pick_combine(p->num_branches), grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  return MLRA_OK;
+}
+
+extern "C" int mlra_decode(const void* q_nope, const void* q_rope, const void* latent_cache, const void* rope_cache,
+                           const int32_t* block_table, const int32_t* seqlens, const float* W_UV, float* out,
+                           const mlra_decode_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+  if (p && p->batch > 0 && (!W_UV || !out)) return set_error(MLRA_ERR_NULL, "W_UV and out must be non-NULL");
+  int rc = mlra_decode_splitkv(q_nope, q_rope, latent_cache, rope_cache, block_table, seqlens, p, workspace,
+                               workspace_bytes, stream);
+  if (rc) return rc;
+  return mlra_decode_combine(seqlens, W_UV, out, p, workspace, workspace_bytes, stream);
+}
+
+extern "C" int mlra_decode_plan(const int32_t* seqlens, int32_t batch, int32_t num_splits, int32_t max_segments,
+                                int32_t* plan, void* stream) {
+  if (batch < 0 || num_splits < 1 || max_segments < 1)
+    return set_error(MLRA_ERR_SHAPE, "batch >= 0, num_splits >= 1 and max_segments >= 1 required");
+  if (!plan || (batch > 0 && !seqlens)) return set_error(MLRA_ERR_NULL, "seqlens and plan must be non-NULL");
+  hipLaunchKernelGGL(plan_kernel, dim3(num_splits), dim3(64), 0, static_cast<hipStream_t>(stream), seqlens, batch,
+                     num_splits, max_segments, plan);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+  return MLRA_OK;
+}
+
+extern "C" int mlra_copy_bandwidth_probe(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return set_error(MLRA_ERR_NULL, "src and dst must be non-NULL");
+  if (!aligned16(src) || !aligned16(dst) || bytes % 16 != 0)
+    return set_error(MLRA_ERR_ALIGN, "src, dst and bytes must be 16-byte aligned");
+  if (bytes == 0) return MLRA_OK;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  const int64_t n = int64_t(bytes / 16);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > int64_t(cus) * 16) blocks = int64_t(cus) * 16;
+  hipLaunchKernelGGL(copy_kernel, dim3(unsigned(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "copy kernel launch");
+  return MLRA_OK;
+}

@@ -1,0 +1,36 @@
+// Shared between the host-only parameter code and the HIP translation unit.
+// Holds no HIP types so that mlra_params.cpp builds as plain C++.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "mlra.h"
+
+namespace mlra {
+
+constexpr int kTile = MLRA_TILE_TOKENS;   // tokens per tile of the split-KV stream
+constexpr int kHeadBlock = 32;            // query heads per MFMA column block
+constexpr int kLatentTotal = 512;         // NB * d_latent in every supported form
+constexpr int kDRope = 64;
+constexpr int kDV = 128;
+
+// Workspace of one decode call: per-split partials, indexed by slot = split + sequence.
+//   part_o  fp32 [slots][NB][h][d_latent]  unnormalised output of one split for one sequence
+//   part_ml fp32 [slots][NB][h][2]         (running max in log2 units, running sum)
+struct WorkspaceLayout {
+  int64_t slots = 0;
+  size_t part_o_off = 0;
+  size_t part_ml_off = 0;
+  size_t total = 0;
+};
+
+WorkspaceLayout workspace_layout(const mlra_decode_params& p, int32_t num_splits);
+
+// Records a thread-local message and returns `code`.
+int set_error(int code, const char* fmt, ...);
+void clear_error();
+
+int head_blocks(int num_heads);
+
+}  // namespace mlra

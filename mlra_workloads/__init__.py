@@ -145,6 +145,25 @@ class DecodeInputs:
     def total_tokens(self) -> int:
         return int(self.seqlens.sum())
 
+    def to(self, device) -> "DecodeInputs":
+        """Copy every tensor to `device`, keeping joint-layout views as views."""
+        mv = lambda t: None if t is None else t.to(device)
+        if self.q_joint is not None:
+            NB, DL = self.w.NB, self.w.DL
+            qj, cj = mv(self.q_joint), mv(self.cache_joint)
+            qn, qr = qj[..., :NB * DL].unflatten(-1, (NB, DL)), qj[..., NB * DL:]
+            lat, rp = cj[:, :NB * DL].unflatten(-1, (NB, DL)), cj[:, NB * DL:]
+        else:
+            qj = cj = None
+            qn, qr, lat, rp = mv(self.q_nope), mv(self.q_rope), mv(self.latent), mv(self.rope)
+        return dataclasses.replace(self, seqlens=mv(self.seqlens), q_nope=qn, q_rope=qr, latent=lat, rope=rp,
+                                   W_UV=mv(self.W_UV), block_table=mv(self.block_table), q_joint=qj,
+                                   cache_joint=cj)
+
+    def cache_bytes(self) -> int:
+        """Bytes of cache one decode step must read: every cached token's latent and RoPE rows."""
+        return self.total_tokens * self.w.token_elems * self.w.elem_bytes
+
 
 def _randn(gen, shape, std, dtype):
     x = torch.randn(*shape, generator=gen, dtype=torch.float32)

@@ -1,0 +1,136 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and the
+host-only validation rejects each kind of bad argument (no GPU needed, no kernel runs)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    from long_context_decode_mlra_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libmlra.so not built (run __graft_entry__.build())")
+    return L
+
+
+def test_header_declares_exactly_the_exported_symbols():
+    L = _lib()
+    header = open(os.path.join(ROOT, "include", "mlra.h")).read()
+    declared = set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(mlra_\w+)\s*\(", header, re.M))
+    assert declared == set(L.EXPORTS)
+    lib = L.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.mlra_abi_version() == 1
+
+
+def test_exports_visible_to_dynamic_loader():
+    L = _lib()
+    raw = ctypes.CDLL(L.LIB_PATH)
+    for name in L.EXPORTS:
+        assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value
+
+
+def good_params(**kw):
+    L = _lib()
+    p = L.DecodeParams()
+    p.batch, p.num_heads, p.num_branches, p.d_latent, p.d_rope, p.d_v = 32, 32, 4, 128, 64, 128
+    p.dtype, p.page_size, p.max_seqlen, p.max_pages_per_seq, p.num_splits, p.reserved = 0, 0, 32768, 0, 512, 0
+    p.q_stride_b, p.q_stride_h, p.qr_stride_b, p.qr_stride_h = 32 * 512, 512, 32 * 64, 64
+    p.lat_stride_tok, p.rope_stride_tok = 512, 64
+    p.sm_scale, p.out_scale = 1 / math.sqrt(192), 0.5
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def rc(p):
+    L = _lib()
+    return L.lib().mlra_check_params(ctypes.byref(p))
+
+
+def test_valid_params_pass():
+    assert rc(good_params()) == 0
+    assert rc(good_params(num_branches=1, d_latent=512, q_stride_h=576, lat_stride_tok=576,
+                          rope_stride_tok=576, qr_stride_h=576, qr_stride_b=32 * 576, q_stride_b=32 * 576)) == 0
+    assert rc(good_params(num_branches=2, d_latent=256)) == 0
+    assert rc(good_params(dtype=1, num_heads=16)) == 0
+    assert rc(good_params(page_size=64, max_pages_per_seq=512)) == 0
+    assert rc(good_params(batch=0)) == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_heads", 0, -3), ("num_heads", 65, -3), ("num_branches", 3, -3), ("d_latent", 64, -3),
+    ("d_rope", 32, -3), ("d_v", 64, -3), ("dtype", 7, -3), ("batch", -1, -2), ("max_seqlen", -5, -2),
+    ("page_size", 48, -3), ("page_size", -64, -2), ("num_splits", -1, -2), ("reserved", 1, -2),
+    ("q_stride_h", 100, -2), ("lat_stride_tok", 500, -2), ("rope_stride_tok", 63, -2),
+    ("q_stride_h", 516, -4), ("lat_stride_tok", 516, -4), ("qr_stride_b", 2052, -4),
+    ("sm_scale", 0.0, -2), ("sm_scale", float("nan"), -2), ("out_scale", float("inf"), -2),
+    ("lat_stride_tok", 1 << 25, -2),
+])
+def test_bad_params_rejected(field, value, code):
+    assert rc(good_params(**{field: value})) == code
+    L = _lib()
+    assert L.lib().mlra_last_error().decode()
+
+
+def test_paged_needs_enough_table_columns():
+    assert rc(good_params(page_size=64, max_pages_per_seq=511)) == -2
+    assert rc(good_params(page_size=64, max_pages_per_seq=512)) == 0
+
+
+def test_null_params():
+    L = _lib()
+    assert L.lib().mlra_check_params(None) == -1
+
+
+def test_workspace_size_with_explicit_splits_needs_no_device():
+    L = _lib()
+    p = good_params(num_splits=512)
+    n = ctypes.c_size_t(0)
+    assert L.lib().mlra_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    slots = 512 + 32
+    expect_o = slots * 32 * 512 * 4
+    expect_ml = slots * 4 * 32 * 2 * 4
+    assert n.value >= expect_o + expect_ml and n.value % 256 == 0 and n.value < expect_o + expect_ml + 1024
+
+
+def test_decode_argument_errors_before_any_launch():
+    """Pointer and workspace checks happen on the host before any HIP call."""
+    L = _lib()
+    lib = L.lib()
+    p = good_params(num_splits=8)
+    fake = ctypes.c_void_p(1 << 20)
+    # workspace too small
+    r = lib.mlra_decode(fake, fake, fake, fake, None, fake, fake, fake, ctypes.byref(p), fake, 256, None)
+    assert r == -5
+    # NULL query pointer
+    n = ctypes.c_size_t(0)
+    lib.mlra_decode_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    r = lib.mlra_decode(None, fake, fake, fake, None, fake, fake, fake, ctypes.byref(p), fake, n.value, None)
+    assert r == -1
+    # misaligned cache pointer
+    r = lib.mlra_decode(fake, fake, ctypes.c_void_p((1 << 20) + 8), fake, None, fake, fake, fake, ctypes.byref(p),
+                        fake, n.value, None)
+    assert r == -4
+    # block_table given for a contiguous cache
+    r = lib.mlra_decode(fake, fake, fake, fake, fake, fake, fake, fake, ctypes.byref(p), fake, n.value, None)
+    assert r == -1
+    # misaligned workspace
+    r = lib.mlra_decode(fake, fake, fake, fake, None, fake, fake, fake, ctypes.byref(p),
+                        ctypes.c_void_p((1 << 20) + 16), n.value, None)
+    assert r == -4
+    assert lib.mlra_decode_plan(fake, 4, 0, 4, fake, None) == -2
+    assert lib.mlra_copy_bandwidth_probe(fake, ctypes.c_void_p((1 << 20) + 4), 64, None) == -4
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from long_context_decode_mlra_amd import _lib as L
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(ImportError):
+        L.lib()
