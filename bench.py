@@ -2,7 +2,7 @@
 """MLRA-4 decode-attention benchmark on one MI355X.
 
 One step = one full decode of the workload's batch through the C ABI
-(split-KV attention kernel + combine/W_UV kernel), inputs resident in HBM.
+(split-KV attention kernel, combine/W_UV kernel, finalize kernel), inputs resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--no-cpu-baseline]
 
@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=1024, help="size of the copy-kernel reference run")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step recorded once as a HIP graph and replayed (reported beside)")
     return ap.parse_args()
 
 
@@ -117,7 +119,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     # Copy-kernel reference (achievable bandwidth; also the calibration kernel for byte counters).
-    copy_gbps = None
+    copy_gbps = read_gbps = None
     if args.copy_probe_mib > 0:
         nbytes = args.copy_probe_mib << 20
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -131,6 +133,15 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         copy_gbps = 2 * nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            mlra.read_bandwidth_probe(src, sink)
+        e0.record(stream)
+        for _ in range(10):
+            mlra.read_bandwidth_probe(src, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        read_gbps = nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         del src, dst
 
     print(f"bench: {args.warmup} warmup + {args.steps} timed steps, splits={dec.splits}", file=sys.stderr, flush=True)
@@ -138,6 +149,7 @@ def main():
         dec(stream)
     torch.cuda.synchronize()
 
+    # Eager launches, with events around the attention kernel and the combine (per-kernel times).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -149,7 +161,20 @@ def main():
         evs[k][2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    eager_ms = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = eager_ms
+    graph_ms = None
+    if args.graph:
+        # The same step recorded once as a HIP graph and replayed: the way a serving loop runs it.
+        graph = dec.capture_graph()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     dk = sorted(e[0].elapsed_time(e[1]) for e in evs)
     ck = sorted(e[1].elapsed_time(e[2]) for e in evs)
     dk_mean = sum(dk) / len(dk)
@@ -175,6 +200,8 @@ def main():
                    "d_latent": w.DL, "d_rope": w.DR, "d_v": w.DV, "seq_len": inp.max_seqlen,
                    "cached_tokens": tokens, "page_size": w.page_size, "num_splits": dec.splits,
                    "parallelism": "none (one GPU)"},
+        "timing": "eager launches through the C ABI, K steps between two device synchronisations",
+        "graph_replay_us_per_step": None if graph_ms is None else round(graph_ms * 1e3, 2),
         "achieved_hbm_TBps": round(ab["step"] / (us * 1e-6) / 1e12, 3),
         "tokens_per_s": round(len(inp.seqlens) / (us * 1e-6), 1),
         "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4),
@@ -183,6 +210,7 @@ def main():
                        "combine_kernel_mean": round(ck_mean * 1e3, 2)},
         "algorithmic_bytes_per_step": ab["step"],
         "copy_probe_GBps": None if copy_gbps is None else round(copy_gbps, 1),
+        "read_probe_GBps": None if read_gbps is None else round(read_gbps, 1),
         "roofline": roofline,
         "cpu_baseline": None,
     }

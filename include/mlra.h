@@ -107,8 +107,9 @@ int mlra_decode_workspace_size(const mlra_decode_params* p, size_t* bytes);
 
 /*
  * Full decode step: split-KV attention (plan, tile stream, per-latent-head
- * online softmax, partials) followed by the combine with the fused W_UV
- * up-projection and branch sum. Two kernel launches on `stream`.
+ * online softmax, partials) followed by the combine: log-sum-exp merge of the
+ * partials with the W_UV up-projection, then the branch sum and output scale.
+ * Three kernel launches on `stream`.
  *
  *   q_nope        [B][h] rows of NB*d_latent elements (strides q_stride_b/h); dtype
  *   q_rope        [B][h] rows of d_rope elements (strides qr_stride_b/h); dtype
@@ -136,8 +137,9 @@ int mlra_decode_splitkv(const void* q_nope, const void* q_rope, const void* late
                         const int32_t* block_table, const int32_t* seqlens, const mlra_decode_params* p,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Second half of mlra_decode alone: log-sum-exp merge of the partials that
- * mlra_decode_splitkv left in `workspace` (same p, same seqlens), then
+/* Second half of mlra_decode alone (two launches): log-sum-exp merge of the
+ * partials that mlra_decode_splitkv left in `workspace` (same p, same seqlens,
+ * same workspace, after it on the same stream), then
  * out[b,i] = out_scale * sum_j obar_j @ W_UV[j,i]. */
 int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, float* out, const mlra_decode_params* p,
                         void* workspace, size_t workspace_bytes, void* stream);
@@ -160,6 +162,11 @@ int mlra_decode_plan(const int32_t* seqlens, int32_t batch, int32_t num_splits, 
  * of 16): the achievable-bandwidth reference and the calibration kernel for the
  * HBM byte counters. */
 int mlra_copy_bandwidth_probe(const void* src, void* dst, size_t bytes, void* stream);
+
+/* Read-only stream over `bytes` bytes of `src` (16-byte aligned, multiple of 16):
+ * the achievable read bandwidth. XORs every word into *sink (device uint32,
+ * caller-initialised), so the reads cannot be dropped. */
+int mlra_read_bandwidth_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 } /* extern "C" */

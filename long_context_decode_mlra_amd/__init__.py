@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import (MLRA_BF16, MLRA_F32, MLRA_MAX_HEADS, MLRA_TILE_TOKENS, DecodeParams, MlraError, check, lib)
 
 __all__ = ["decode", "decode_splitkv", "decode_combine", "make_params", "Decoder", "workspace_size", "num_splits",
-           "check_params", "plan", "copy_bandwidth_probe", "MlraError", "DecodeParams", "MLRA_BF16", "MLRA_F32",
+           "check_params", "plan", "copy_bandwidth_probe", "read_bandwidth_probe", "MlraError", "DecodeParams", "MLRA_BF16", "MLRA_F32",
            "MLRA_TILE_TOKENS", "MLRA_MAX_HEADS", "lib"]
 
 _DTYPES = {torch.bfloat16: MLRA_BF16, torch.float32: MLRA_F32}
@@ -114,6 +114,19 @@ class Decoder:
         check(lib().mlra_decode_splitkv(_ptr(qn), _ptr(qr), _ptr(lat), _ptr(rp), _ptr(bt), _ptr(sl),
                                         ctypes.byref(self.p), _ptr(self.workspace), self.ws_bytes, _stream(stream)))
 
+    def capture_graph(self) -> "torch.cuda.CUDAGraph":
+        """Record one full decode step (all kernel launches of mlra_decode) into a HIP graph.
+        Replaying it re-runs the step on the same tensors; it records kernel launches only."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm-up launch outside the capture
+            self(side)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self()
+        return graph
+
     def combine(self, stream=None) -> torch.Tensor:
         sl, W = self.tensors[5], self.tensors[6]
         check(lib().mlra_decode_combine(_ptr(sl), _ptr(W), _ptr(self.out), ctypes.byref(self.p),
@@ -152,3 +165,9 @@ def copy_bandwidth_probe(src: torch.Tensor, dst: torch.Tensor, stream=None) -> N
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst smaller than src")
     check(lib().mlra_copy_bandwidth_probe(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def read_bandwidth_probe(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """XOR-reduce every 16-byte word of `src` into sink[0] (int32, device)."""
+    nbytes = src.numel() * src.element_size()
+    check(lib().mlra_read_bandwidth_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)))

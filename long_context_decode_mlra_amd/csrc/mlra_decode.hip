@@ -16,8 +16,9 @@
 //                   query heads of the split's sequence, keeps an fp32 online
 //                   softmax per (latent head, query head), and writes one partial
 //                   (unnormalised O, running max, running sum) per sequence it touches.
-//   combine_kernel  log-sum-exp merge of a sequence's partials, then the fused
-//                   W_UV up-projection, branch sum and output scale.
+//   combine_kernel  log-sum-exp merge of each sequence's split partials and the W_UV
+//                   up-projection on fp32 MFMA, per 128-channel block of the latent.
+//   finalize_kernel the branch sum of the projected blocks and the output scale.
 // Splitting is balanced over the flattened tiles of all sequences (the plan).
 #include <hip/hip_runtime.h>
 
@@ -116,6 +117,25 @@ __device__ void find_sequence(const int32_t* __restrict__ seqlens, int B, int64_
   P_out = carry;
 }
 
+// prefix[b] = first global tile of sequence b (b <= B), prefix[B+1] = T, prefix[B+2] = G.
+// Called by one whole wave.
+__device__ void write_prefix(const int32_t* __restrict__ seqlens, int B, const Plan& p, int64_t* prefix) {
+  const int lane = threadIdx.x & 63;
+  int64_t carry = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    const int64_t t = b < B ? tiles_of(seqlens[b]) : 0;
+    const int64_t incl = wave_inclusive_scan(t);
+    if (b < B) prefix[b] = carry + incl - t;
+    carry += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) {
+    prefix[B] = carry;
+    prefix[B + 1] = p.T;
+    prefix[B + 2] = p.G;
+  }
+}
+
 struct SegmentWalk {
   int b;       // current sequence
   int64_t Pb;  // its first global tile
@@ -171,6 +191,7 @@ struct DecodeArgs {
   const int32_t* seqlens;
   float* part_o;
   float* part_ml;
+  int64_t* prefix;  // [B + 3]: first global tile of each sequence, then T, T, G (written by workgroup 0)
   int B, h, G_req, page_size, max_seqlen, max_pages;
   int64_t q_sb, q_sh, qr_sb, qr_sh;  // bytes
   int64_t lat_stride, rope_stride;   // bytes
@@ -452,6 +473,7 @@ void decode_kernel(DecodeArgs a) {
 
   const Plan plan = make_plan(a.seqlens, a.B, a.G_req);
   const int g = blockIdx.x;
+  if (g == 0 && wave == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
   if (g >= plan.G) return;
   SegmentWalk walk = begin_walk(a.seqlens, a.B, g, plan);
 
@@ -564,93 +586,191 @@ void decode_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ combine kernel
+//
+// One workgroup per (query head i, 128-channel block q of the 512 latent channels,
+// group of up to 32 sequences). Block q lies in latent head j = q / (4/NB), channels
+// c0..c0+127 of it, c0 = (q % (4/NB)) * 128.
+//  1. merge:   obar[b][k] = sum_s 2^{m_s-M} O_s[c0+k] / sum_s 2^{m_s-M} l_s over the splits
+//              s holding part of sequence b (slots g + b, g in [g_first, g_last]), into LDS.
+//  2. project: y_q[b][d] = sum_k obar[b][k] * W_UV[j][i][c0+k][d] on fp32 MFMA
+//              (M = sequences, N = 128 output channels, K = 128). Every W_UV row is read
+//              by exactly one workgroup of the grid.
+//  y_q goes to the workspace; finalize_kernel adds the four blocks in the fixed order
+//  q = 0..3 (the branch sum) and applies out_scale. (Summing inside this kernel would need
+//  device-scope fences between workgroups on different L2 slices; their write-back and
+//  invalidate cost more than the extra launch.)
 
 struct CombineArgs {
-  const int32_t* seqlens;
   const float* part_o;
   const float* part_ml;
+  const int64_t* prefix;
   const float* W_UV;
-  float* out;
-  int B, h, G_req;
-  float out_scale;
+  float* ypart;    // [groups][h][4][32][128]
+  int B, h;
 };
 
-constexpr int kCombineSeqs = 4;  // sequences per combine workgroup (W_UV rows reused across them)
+constexpr int kCombSeqs = 32;
+
+struct MergeState {
+  float M, den;
+  floatx4 acc[4];
+};
+
+// Fold one unnormalised partial (max m, sum l, four channel quads o) into st.
+__device__ __forceinline__ void merge_in(MergeState& st, float m, float l, const floatx4 (&o)[4]) {
+  if (m == -INFINITY) return;
+  if (m > st.M) {
+    const float sc = __builtin_amdgcn_exp2f(st.M - m);  // 0 when st.M is -inf
+    st.den *= sc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) st.acc[u] *= sc;
+    st.M = m;
+  }
+  const float w = __builtin_amdgcn_exp2f(m - st.M);
+  st.den = fmaf(w, l, st.den);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) st.acc[u] += w * o[u];
+}
 
 template <int NB>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  constexpr int WPB = 4 / NB;
   constexpr int DL = kLatentTotal / NB;
-  __shared__ float obar[kCombineSeqs][kLatentTotal];
-  __shared__ long long sP[kCombineSeqs + 1];
-  __shared__ long long sT;
-  __shared__ int sG;
+  constexpr int kBatch = 4;  // slots loaded together
+  __shared__ float ob[128][kCombSeqs];  // merged block, k-major: ob[k][b]
+  __shared__ float st_red[18 * 256];     // per (slot part, pair): M, den, acc[16] (only when parts > 1)
 
   const int tid = threadIdx.x;
-  const int i = blockIdx.x;  // query head
-  const int b0 = blockIdx.y * kCombineSeqs;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int i = blockIdx.x;
+  const int q = blockIdx.y;
+  const int grp = blockIdx.z;
+  const int j = q / WPB;
+  const int c0 = (q % WPB) * 128;
+  const int b0 = grp * kCombSeqs;
+  const int nb = min(kCombSeqs, a.B - b0);
+  const int n = lane & 31, hh = lane >> 5;
 
-  if (tid < 64) {
-    const Plan plan = make_plan(a.seqlens, a.B, a.G_req);
-    int64_t carry = 0;
-    for (int base = 0; base < a.B; base += 64) {
-      const int b = base + tid;
-      const int64_t t = b < a.B ? tiles_of(a.seqlens[b]) : 0;
-      const int64_t incl = wave_inclusive_scan(t);
-      if (b < a.B && b >= b0 && b < b0 + kCombineSeqs) {
-        sP[b - b0] = carry + incl - t;
-        sP[b - b0 + 1] = carry + incl;
-      }
-      carry += __shfl(incl, 63, 64);
-    }
-    if (tid == 0) {
-      sT = plan.T;
-      sG = plan.G;
-    }
-  }
-  __syncthreads();
-  const Plan plan{sT, sG};
-
-  for (int bl = 0; bl < kCombineSeqs; ++bl) {
-    const int b = b0 + bl;
-    if (b >= a.B) break;
-    const int64_t P0 = sP[bl], P1 = sP[bl + 1];
+  // The W_UV slice this wave multiplies by (rows c0 + 2kb + hh, column 32*wave + n), issued
+  // first so that the loads overlap the merge.
+  const float* wcol = a.W_UV + ((int64_t(j) * a.h + i) * DL + c0) * kDV + 32 * wave + n;
+  float wv[64];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      const int kk = tid + 256 * h2;
-      const int j = kk / DL, c = kk % DL;
-      float v = 0.f;
-      if (P1 > P0) {
-        const int64_t gf = split_of_tile(P0, plan), gl = split_of_tile(P1 - 1, plan);
-        float M = -INFINITY;
-        for (int64_t gg = gf; gg <= gl; ++gg) M = fmaxf(M, a.part_ml[(((gg + b) * NB + j) * a.h + i) * 2]);
-        float num = 0.f, den = 0.f;
-        for (int64_t gg = gf; gg <= gl; ++gg) {
-          const int64_t r = ((gg + b) * NB + j) * a.h + i;
-          const float w = __builtin_amdgcn_exp2f(a.part_ml[r * 2] - M);
-          num = fmaf(w, a.part_o[r * DL + c], num);
-          den = fmaf(w, a.part_ml[r * 2 + 1], den);
+  for (int kb = 0; kb < 64; ++kb) wv[kb] = wcol[(2 * kb + hh) * kDV];
+  __builtin_amdgcn_sched_barrier(0);
+
+  const Plan plan{a.prefix[a.B + 1], int(a.prefix[a.B + 2])};
+
+  // ---- 1. merge. Eight threads per sequence, each owning channel quads cq0 + 8v (v < 4);
+  // with nbp = nb rounded up to a power of two, S = 32 / nbp slot parts share a sequence.
+  int nbp = 1;
+  while (nbp < nb) nbp <<= 1;
+  const int NPP = nbp * 8;  // threads per slot part
+  const int S = 256 / NPP;
+  const int r = tid / NPP;
+  const int rem = tid % NPP;
+  const int bl = rem / 8;
+  const int cq0 = rem % 8;
+  const bool live = bl < nb;
+  const int b = b0 + (live ? bl : 0);
+
+  MergeState st;
+  st.M = -INFINITY;
+  st.den = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) st.acc[u] = floatx4{};
+  if (live) {
+    const int64_t P0 = a.prefix[b], P1 = a.prefix[b + 1];
+    if (P1 > P0) {
+      const int64_t gf = split_of_tile(P0, plan), gl = split_of_tile(P1 - 1, plan);
+      for (int64_t g = gf + r; g <= gl; g += kBatch * S) {
+        floatx2 ml[kBatch];
+        floatx4 o[kBatch][4];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int64_t gg = g + int64_t(u) * S;
+          const int64_t row = ((min(gg, gl) + b) * NB + j) * a.h + i;
+          ml[u] = *reinterpret_cast<const floatx2*>(a.part_ml + row * 2);
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            o[u][v] = *reinterpret_cast<const floatx4*>(a.part_o + row * DL + c0 + 4 * (cq0 + 8 * v));
+          if (gg > gl) ml[u][0] = -INFINITY;  // past the end: re-read the last slot, then skip it
         }
-        v = num / den;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) merge_in(st, ml[u][0], ml[u][1], o[u]);
       }
-      obar[bl][kk] = v;
     }
   }
+  if (S > 1) {
+    // Part r, field f (M, den, 16 accumulators), pair rem at st_red[(r * 18 + f) * NPP + rem].
+    if (live) {
+      st_red[(r * 18 + 0) * NPP + rem] = st.M;
+      st_red[(r * 18 + 1) * NPP + rem] = st.den;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st_red[(r * 18 + 2 + 4 * u + e) * NPP + rem] = st.acc[u][e];
+    }
+    __syncthreads();
+    if (live && r == 0) {
+      for (int rr = 1; rr < S; ++rr) {  // fixed order: part 0, 1, 2, ...
+        const float* sr = st_red + rr * 18 * NPP + rem;
+        floatx4 o1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o1[u] = floatx4{sr[(2 + 4 * u) * NPP], sr[(3 + 4 * u) * NPP], sr[(4 + 4 * u) * NPP], sr[(5 + 4 * u) * NPP]};
+        // Each part is an unnormalised partial of the same form as a split's.
+        merge_in(st, sr[0], sr[NPP], o1);
+      }
+    }
+  }
+  if (r == 0) {
+    const float inv = (live && st.den > 0.f) ? 1.f / st.den : 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int k = 4 * (cq0 + 8 * v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ob[k + e][bl] = live ? st.acc[v][e] * inv : 0.f;
+    }
+  }
+  // Sequences of the padded group beyond nbp read as zero.
+  for (int idx = tid; idx < 128 * kCombSeqs; idx += 256)
+    if ((idx % kCombSeqs) >= nbp) ob[idx / kCombSeqs][idx % kCombSeqs] = 0.f;
   __syncthreads();
 
-  // out[b, i, d] = out_scale * sum_k obar[b][k] * W_UV[j(k), i, c(k), d], k = j*DL + c.
-  const int d = tid & 127;
-  const int bl0 = tid >> 7;  // this thread covers sequences bl0 and bl0 + 2
-  float acc0 = 0.f, acc1 = 0.f;
-  for (int j = 0; j < NB; ++j) {
-    const float* w = a.W_UV + ((int64_t(j) * a.h + i) * DL) * kDV + d;
-    for (int c = 0; c < DL; ++c) {
-      const float wv = w[int64_t(c) * kDV];
-      acc0 = fmaf(obar[bl0][j * DL + c], wv, acc0);
-      acc1 = fmaf(obar[bl0 + 2][j * DL + c], wv, acc1);
-    }
-  }
-  if (b0 + bl0 < a.B) a.out[(int64_t(b0 + bl0) * a.h + i) * kDV + d] = a.out_scale * acc0;
-  if (b0 + bl0 + 2 < a.B) a.out[(int64_t(b0 + bl0 + 2) * a.h + i) * kDV + d] = a.out_scale * acc1;
+  // ---- 2. project: wave w computes output channels [32w, 32w+32) for all 32 sequences.
+  floatx16 y = {};
+#pragma unroll
+  for (int kb = 0; kb < 64; ++kb) y = __builtin_amdgcn_mfma_f32_32x32x2f32(ob[2 * kb + hh][n], wv[kb], y, 0, 0, 0);
+
+  float* yq = a.ypart + ((int64_t(grp) * a.h + i) * 4 + q) * (kCombSeqs * kDV);
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) yq[(8 * (rr >> 2) + 4 * hh + (rr & 3)) * kDV + 32 * wave + n] = y[rr];
+}
+
+// out[b][i][:] = out_scale * (y_0 + y_1 + y_2 + y_3)[b][:], blocks added in this order.
+struct FinalizeArgs {
+  const float* ypart;
+  float* out;
+  int B, h;
+  float out_scale;
+};
+
+__global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
+  const int64_t n4 = int64_t(a.B) * a.h * (kDV / 4);
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= n4) return;
+  const int d4 = int(idx % (kDV / 4));
+  const int64_t bi = idx / (kDV / 4);
+  const int i = int(bi % a.h);
+  const int b = int(bi / a.h);
+  const int grp = b / kCombSeqs, bl = b % kCombSeqs;
+  const floatx4* y = reinterpret_cast<const floatx4*>(a.ypart + ((int64_t(grp) * a.h + i) * 4) * (kCombSeqs * kDV) +
+                                                      bl * kDV) + d4;
+  constexpr int kBlk = kCombSeqs * kDV / 4;
+  const floatx4 v = ((y[0] + y[kBlk]) + y[2 * kBlk]) + y[3 * kBlk];
+  reinterpret_cast<floatx4*>(a.out)[idx] = a.out_scale * v;
 }
 
 // ------------------------------------------------------------------ plan dump and copy probe
@@ -677,6 +797,22 @@ __global__ __launch_bounds__(64) void plan_kernel(const int32_t* seqlens, int B,
     }
     ++k;
   }
+}
+
+// Read-only stream: XOR of every 16-byte word, folded into sink[0] once per wave.
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n, uint32_t* sink) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  u32x4 x = {};
+  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const u32x4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+    x ^= v0 ^ v1 ^ v2 ^ v3;
+  }
+  for (; i < n; i += stride) x ^= src[i];
+  uint32_t r = x[0] ^ x[1] ^ x[2] ^ x[3];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) r ^= __shfl_xor(r, off, 64);
+  if ((threadIdx.x & 63) == 0) atomicXor(sink, r);
 }
 
 __global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
@@ -821,6 +957,7 @@ extern "C" int mlra_decode_splitkv(const void* q_nope, const void* q_rope, const
   a.seqlens = seqlens;
   a.part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + lay.part_o_off);
   a.part_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + lay.part_ml_off);
+  a.prefix = reinterpret_cast<int64_t*>(static_cast<unsigned char*>(workspace) + lay.prefix_off);
   a.B = p->batch;
   a.h = p->num_heads;
   a.G_req = G;
@@ -853,20 +990,30 @@ extern "C" int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, fl
   if (rc) return rc;
   if (p->batch == 0) return MLRA_OK;
   if (!W_UV || !out) return set_error(MLRA_ERR_NULL, "W_UV and out must be non-NULL");
-  CombineArgs a;
-  a.seqlens = seqlens;
-  a.part_o = reinterpret_cast<const float*>(static_cast<unsigned char*>(workspace) + lay.part_o_off);
-  a.part_ml = reinterpret_cast<const float*>(static_cast<unsigned char*>(workspace) + lay.part_ml_off);
-  a.W_UV = W_UV;
-  a.out = out;
-  a.B = p->batch;
-  a.h = p->num_heads;
-  a.G_req = G;
-  a.out_scale = p->out_scale;
-  const dim3 grid(p->num_heads, (p->batch + kCombineSeqs - 1) / kCombineSeqs);
-  hipLaunchKernelGGL(pick_combine(p->num_branches), grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
-  const hipError_t e = hipGetLastError();
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  CombineArgs c;
+  c.part_o = reinterpret_cast<const float*>(ws + lay.part_o_off);
+  c.part_ml = reinterpret_cast<const float*>(ws + lay.part_ml_off);
+  c.prefix = reinterpret_cast<const int64_t*>(ws + lay.prefix_off);
+  c.W_UV = W_UV;
+  c.ypart = reinterpret_cast<float*>(ws + lay.ypart_off);
+  c.B = p->batch;
+  c.h = p->num_heads;
+  const dim3 grid(p->num_heads, 4, (p->batch + kCombSeqs - 1) / kCombSeqs);
+  hipLaunchKernelGGL(pick_combine(p->num_branches), grid, dim3(256), 0, static_cast<hipStream_t>(stream), c);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  FinalizeArgs f;
+  f.ypart = c.ypart;
+  f.out = out;
+  f.B = p->batch;
+  f.h = p->num_heads;
+  f.out_scale = p->out_scale;
+  const int64_t n4 = int64_t(p->batch) * p->num_heads * (kDV / 4);
+  hipLaunchKernelGGL(finalize_kernel, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), f);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "finalize kernel launch");
   return MLRA_OK;
 }
 
@@ -889,6 +1036,24 @@ extern "C" int mlra_decode_plan(const int32_t* seqlens, int32_t batch, int32_t n
                      num_splits, max_segments, plan);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
+  return MLRA_OK;
+}
+
+extern "C" int mlra_read_bandwidth_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+  if (!src || !sink) return set_error(MLRA_ERR_NULL, "src and sink must be non-NULL");
+  if (!aligned16(src) || bytes % 16 != 0) return set_error(MLRA_ERR_ALIGN, "src and bytes must be 16-byte aligned");
+  if (bytes == 0) return MLRA_OK;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  const int64_t n = int64_t(bytes / 16);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > int64_t(cus) * 8) blocks = int64_t(cus) * 8;
+  hipLaunchKernelGGL(read_kernel, dim3(unsigned(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), n, sink);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "read kernel launch");
   return MLRA_OK;
 }
 

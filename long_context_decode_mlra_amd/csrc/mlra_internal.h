@@ -15,13 +15,19 @@ constexpr int kLatentTotal = 512;         // NB * d_latent in every supported fo
 constexpr int kDRope = 64;
 constexpr int kDV = 128;
 
-// Workspace of one decode call: per-split partials, indexed by slot = split + sequence.
+// Workspace of one decode call:
 //   part_o  fp32 [slots][NB][h][d_latent]  unnormalised output of one split for one sequence
+//                                          (slot = split + sequence)
 //   part_ml fp32 [slots][NB][h][2]         (running max in log2 units, running sum)
+//   prefix  int64 [B + 3]                  first tile of each sequence, then T (total tiles), T, G
+//   ypart   fp32 [groups][h][4][32][d_v]   projected 128-channel blocks of up to 32 sequences
+// groups = ceil(B / 32).
 struct WorkspaceLayout {
   int64_t slots = 0;
   size_t part_o_off = 0;
   size_t part_ml_off = 0;
+  size_t prefix_off = 0;
+  size_t ypart_off = 0;
   size_t total = 0;
 };
 

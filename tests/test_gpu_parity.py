@@ -166,13 +166,20 @@ def test_plan_partitions_tiles():
         assert seen == [(b, t) for b in range(B) for t in range(tiles[b])]
 
 
-def test_copy_probe():
+def test_copy_and_read_probes():
     mlra = _mlra()
     src = torch.randn(1 << 20, device="cuda")
     dst = torch.empty_like(src)
     mlra.copy_bandwidth_probe(src, dst)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+    words = torch.randint(-2**31, 2**31 - 1, (1 << 20,), dtype=torch.int32)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mlra.read_bandwidth_probe(words.cuda(), sink)
+    expect = 0
+    for v in words.numpy().view(np.uint32).reshape(-1, 4).T:
+        expect ^= int(np.bitwise_xor.reduce(v))
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == expect
 
 
 # ----------------------------------------------------------------- full-size workloads, sampled sequences
@@ -191,3 +198,46 @@ def test_full_size_sampled(cfg):
     ref = oracle.decode_inputs(inp, batch_indices=sel)
     assert np.all(np.isfinite(got))
     assert_parity(got[list(sel)], ref, label=f"cfg{cfg} sampled {sel}")
+
+
+def test_two_sequence_groups_and_workspace_reuse():
+    """B=40: one full group of 32 sequences and a partial one; the same Decoder (workspace,
+    arrival counters) is called three times in a row and must give the same bits."""
+    mlra = _mlra()
+    rng = np.random.default_rng(40)
+    Ls = tuple(int(x) for x in rng.integers(0, 900, size=40))
+    w = CONFIGS[2].replace(B=40, lengths=("list", Ls))
+    inp = make_inputs(w, seed=40, poison=True)
+    d = inp.to("cuda")
+    dec = mlra.Decoder(d.q_nope, d.q_rope, d.latent, d.rope, seqlens=d.seqlens, W_UV=d.W_UV, sm_scale=w.sm_scale,
+                       out_scale=w.gamma, max_seqlen=inp.max_seqlen)
+    outs = []
+    for _ in range(3):
+        outs.append(dec().cpu().double().numpy())
+        torch.cuda.synchronize()
+    ref = oracle.decode_inputs(inp)
+    assert_parity(outs[0], ref, label="B=40")
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_graph_replay_matches_eager():
+    """A captured decode step replayed several times, with eager work in between, gives the
+    eager result every time (the step records kernel launches only)."""
+    mlra = _mlra()
+    w = CONFIGS[5].replace(B=6, lengths=("list", (700, 1, 2048, 65, 0, 333)))
+    inp = make_inputs(w, seed=12)
+    d = inp.to("cuda")
+    dec = mlra.Decoder(d.q_nope, d.q_rope, d.latent, d.rope, seqlens=d.seqlens, W_UV=d.W_UV, sm_scale=w.sm_scale,
+                       out_scale=w.gamma, max_seqlen=inp.max_seqlen, block_table=d.block_table,
+                       page_size=w.page_size)
+    eager = dec().clone()
+    torch.cuda.synchronize()
+    graph = dec.capture_graph()
+    for k in range(4):
+        dec.out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.out, eager), f"replay {k}"
+        junk = torch.randn(1 << 16, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+    assert_parity(eager.cpu().double().numpy(), oracle.decode_inputs(inp), label="graph")
