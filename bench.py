@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=1024, help="size of the copy-kernel reference run")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "benchmark into the per-launch HBM traffic record under profiles/")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step recorded once as a HIP graph and replayed (reported beside)")
     return ap.parse_args()
@@ -68,6 +71,41 @@ def traffic_record(workload_name):
     return rec
 
 
+def record_traffic(fetch_csv, write_csv, args):
+    """Scale the decode kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same
+    counters read for the copy kernel, whose bytes are known (copy_probe_mib read + written)."""
+    import csv
+    from mlra_workloads import CONFIGS, make_inputs
+
+    def means(path):
+        acc = {}
+        for r in csv.DictReader(open(path)):
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    f, wr = means(fetch_csv), means(write_csv)
+    pick = lambda d, key: next(v for k, v in d.items() if key in k)
+    copy_bytes = args.copy_probe_mib << 20
+    f_scale = copy_bytes / (pick(f, "copy_kernel") * 1024)
+    w_scale = copy_bytes / (pick(wr, "copy_kernel") * 1024)
+    w = CONFIGS[args.config]
+    inp = make_inputs(w, seed=args.config)
+    fetch = pick(f, "decode_kernel") * 1024 * f_scale
+    write = pick(wr, "decode_kernel") * 1024 * w_scale
+    ab = algorithmic_bytes(inp)
+    src = open(os.path.join(ROOT, "long_context_decode_mlra_amd", "csrc", "mlra_decode.hip"), "rb").read()
+    rec = {"workload": w.name, "kernel": "decode_kernel", "fetch_bytes_per_launch": round(fetch),
+           "write_bytes_per_launch": round(write), "hbm_bytes_per_launch": round(fetch + write),
+           "algorithmic_bytes_per_launch": ab["decode_kernel"],
+           "traffic_over_algorithmic": round((fetch + write) / ab["decode_kernel"], 4),
+           "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+           "calibration": f"copy_kernel of {copy_bytes} bytes read and written in the same runs",
+           "kernel_source_sha256": hashlib.sha256(src).hexdigest()}
+    out = os.path.join(ROOT, "profiles", f"traffic_decode_{w.name}.json")
+    json.dump(rec, open(out, "w"), indent=1)
+    print(json.dumps(rec))
+
+
 def cpu_baseline(inp, target_s):
     import numpy as np  # noqa: F401
     import oracle
@@ -95,6 +133,9 @@ def cpu_baseline(inp, target_s):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic, args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for {max(args.gpus, world)}); "

@@ -163,8 +163,9 @@ int mlra_decode_plan(const int32_t* seqlens, int32_t batch, int32_t num_splits, 
  * HBM byte counters. */
 int mlra_copy_bandwidth_probe(const void* src, void* dst, size_t bytes, void* stream);
 
-/* Read-only stream over `bytes` bytes of `src` (16-byte aligned, multiple of 16):
- * the achievable read bandwidth. XORs every word into *sink (device uint32,
+/* Read-only stream over `bytes` bytes of `src` (16-byte aligned, multiple of 16)
+ * with non-temporal loads, one contiguous chunk per workgroup: the achievable
+ * streaming-read bandwidth. XORs every word into *sink (device uint32,
  * caller-initialised), so the reads cannot be dropped. */
 int mlra_read_bandwidth_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
 

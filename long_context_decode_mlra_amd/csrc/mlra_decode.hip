@@ -805,16 +805,24 @@ __global__ __launch_bounds__(64) void plan_kernel(const int32_t* seqlens, int B,
   }
 }
 
-// Read-only stream: XOR of every 16-byte word, folded into sink[0] once per wave.
-__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n, uint32_t* sink) {
-  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+// Read-only stream: each workgroup reads one contiguous chunk with non-temporal 16-byte
+// loads, 16 per thread in flight; the XOR of every word goes to sink[0] once per wave.
+constexpr int kReadUnroll = 16;
+
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n, int64_t per_wg,
+                                                   uint32_t* sink) {
+  const int64_t begin = int64_t(blockIdx.x) * per_wg;
+  const int64_t end = begin + per_wg < n ? begin + per_wg : n;
   u32x4 x = {};
-  int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const u32x4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
-    x ^= v0 ^ v1 ^ v2 ^ v3;
+  int64_t i = begin + threadIdx.x;
+  for (; i + (kReadUnroll - 1) * 256 < end; i += kReadUnroll * 256) {
+    u32x4 v[kReadUnroll];
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < kReadUnroll; ++u) x ^= v[u];
   }
-  for (; i < n; i += stride) x ^= src[i];
+  for (; i < end; i += 256) x ^= __builtin_nontemporal_load(src + i);
   uint32_t r = x[0] ^ x[1] ^ x[2] ^ x[3];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) r ^= __shfl_xor(r, off, 64);
@@ -1054,10 +1062,10 @@ extern "C" int mlra_read_bandwidth_probe(const void* src, size_t bytes, uint32_t
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "device query");
   const int64_t n = int64_t(bytes / 16);
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > int64_t(cus) * 8) blocks = int64_t(cus) * 8;
+  const int64_t blocks = int64_t(cus) * 4;
+  const int64_t per_wg = (n + blocks - 1) / blocks;
   hipLaunchKernelGGL(read_kernel, dim3(unsigned(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const u32x4*>(src), n, sink);
+                     static_cast<const u32x4*>(src), n, per_wg, sink);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "read kernel launch");
   return MLRA_OK;
