@@ -44,6 +44,28 @@ constexpr float kLog2e = 1.4426950408889634f;
 // step, so allocating it in L2 / the Infinity Cache only evicts useful lines; streaming
 // loads measured about 7 TB/s against about 6.1 TB/s for default-policy loads on MI355X.
 constexpr int kStreamPolicy = 2;
+
+#ifndef MLRA_DMA_STAGES
+#define MLRA_DMA_STAGES 2
+#endif
+
+// Wave-uniform read of read-only metadata through the scalar data cache. Scalar loads
+// are counted by lgkmcnt, so they never wait on the tile loads in flight.
+__device__ __forceinline__ int32_t scalar_read(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
+// Wait until at most n of this wave's vector-memory operations are outstanding
+// (n is a small compile-time-bounded count; s_waitcnt takes an immediate).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+    case 27: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
 // A running max is only raised once the tile max exceeds it by this many
 // log2 units, so exp2 arguments stay <= 8 and unneeded rescales are skipped.
 // The final result is exact either way: numerator and denominator share the max.
@@ -219,12 +241,17 @@ struct Geo {
   static constexpr int kInstPerWave = (kInst + kWaves - 1) / kWaves;
   static constexpr int kWPB = 4 / NB;  // waves sharing one latent head (each owns 128 channels)
   static constexpr int kDL = kLatentTotal / NB;
-  static constexpr int kLds = 2 * kTileBytes;
   // Loads go straight into LDS unless the idle tile buffer is needed for the
   // logit exchange between the waves that share one latent head.
   static constexpr bool kDirect = (kWPB == 1);
+  // Tile buffers: with direct loads, one bf16 head block (every wave issues the same
+  // number of loads per tile) runs a deeper ring: kStages - 1 tiles in flight.
+  static constexpr int kStages = (kDirect && kEsz == 2 && HB == 1) ? MLRA_DMA_STAGES : 2;
+  static constexpr int kLds = kStages * kTileBytes;
   static_assert(kLatTile % 1024 == 0 && kTileBytes % 1024 == 0, "tile must be whole 1 KiB loads");
   static_assert(kWaves * 4096 <= kTileBytes, "logit exchange must fit the idle tile buffer");
+  static_assert(kStages == 2 || (kInstPerWave * kWaves == kInst && kInstPerWave == 9 && kStages <= 4),
+                "deep rings need equal per-wave load counts that wait_vmcnt knows");
 };
 
 // Per-lane MFMA operands of the query: lane (n, hh) supplies query head 32*hb + n.
@@ -286,7 +313,7 @@ __device__ __forceinline__ TileRows tile_rows(const DecodeArgs& a, int b, int L,
   int64_t row0;
   if (a.block_table) {
     // Pages hold a multiple of kTile tokens, so a tile never straddles two pages.
-    const int page = a.block_table[int64_t(b) * a.max_pages + tok0 / a.page_size];
+    const int page = scalar_read(a.block_table + int64_t(b) * a.max_pages + tok0 / a.page_size);
     row0 = int64_t(page) * a.page_size + tok0 % a.page_size;
   } else {
     row0 = int64_t(b) * a.max_seqlen + tok0;
@@ -460,7 +487,8 @@ __device__ __forceinline__ void tile_pv(const unsigned char* buf, int wq, int n,
 }
 
 template <typename T, int NB, int HB>
-__global__ __attribute__((amdgpu_flat_work_group_size(1, 256 * HB), amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(1, 256 * HB),
+                          amdgpu_waves_per_eu((sizeof(T) == 2 && Geo<T, NB, HB>::kStages == 2) ? 2 : 1, 2)))
 void decode_kernel(DecodeArgs a) {
   using G = Geo<T, NB, HB>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::kLds];
@@ -485,25 +513,40 @@ void decode_kernel(DecodeArgs a) {
 
   int b, ta, te;
   while (next_segment(a.seqlens, a.B, walk, b, ta, te)) {
-    const int L = a.seqlens[b];
+    // Segment bounds are the same in every lane: keep them (and the loop) scalar.
+    b = __builtin_amdgcn_readfirstlane(b);
+    ta = __builtin_amdgcn_readfirstlane(ta);
+    te = __builtin_amdgcn_readfirstlane(te);
+    const int L = scalar_read(a.seqlens + b);
     QOps<T, NB> q;
     load_q<T, NB, HB>(a, b, head, head_ok, wq, sub, hh, q);
     floatx16 O[4] = {};
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    // Two LDS tile buffers; tile k+1 is in flight (in registers, or already on its way
-    // into the other buffer) while tile k is computed.
+    // kStages LDS tile buffers. Direct loads: tiles k+1 .. k+kStages-1 are on their way
+    // into the other buffers while tile k is computed. Register staging: tile k+1 is in
+    // registers while tile k is computed.
     [[maybe_unused]] u32x4 stg[G::kDirect ? 1 : G::kInstPerWave];
-    if constexpr (G::kDirect) issue_tile_dma<T, NB, HB>(a, b, L, ta, wave, lane, smem);
-    else issue_tile_loads<T, NB, HB>(a, b, L, ta, wave, lane, stg);
+    if constexpr (G::kDirect) {
+#pragma unroll
+      for (int st = 0; st < G::kStages - 1; ++st)
+        if (ta + st < te) issue_tile_dma<T, NB, HB>(a, b, L, ta + st, wave, lane, smem + st * G::kTileBytes);
+    } else {
+      issue_tile_loads<T, NB, HB>(a, b, L, ta, wave, lane, stg);
+    }
     for (int k = ta; k < te; ++k) {
-      unsigned char* buf = smem + ((k - ta) & 1) * G::kTileBytes;
-      unsigned char* idle = smem + (((k - ta) & 1) ^ 1) * G::kTileBytes;
+      const int slot = (k - ta) % G::kStages;
+      unsigned char* buf = smem + slot * G::kTileBytes;
+      unsigned char* idle = smem + ((k - ta + 1) % G::kStages) * G::kTileBytes;
       if constexpr (G::kDirect) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile k has landed
+        // This wave's loads of tile k have landed once at most the later tiles' loads are pending.
+        const int later = min(G::kStages - 2, te - 1 - k);
+        wait_vmcnt(G::kStages == 2 ? 0 : later * G::kInstPerWave);
         lds_barrier();  // every wave's part landed; every wave is done with tile k-1's buffer
-        if (k + 1 < te) issue_tile_dma<T, NB, HB>(a, b, L, k + 1, wave, lane, idle);
+        if (k + G::kStages - 1 < te)
+          issue_tile_dma<T, NB, HB>(a, b, L, k + G::kStages - 1, wave, lane,
+                                    smem + ((k - ta + G::kStages - 1) % G::kStages) * G::kTileBytes);
       } else {
         store_tile<T, NB, HB>(buf, wave, lane, stg);
         if (k + 1 < te) issue_tile_loads<T, NB, HB>(a, b, L, k + 1, wave, lane, stg);
@@ -572,10 +615,10 @@ void decode_kernel(DecodeArgs a) {
     lds_barrier();  // both tile buffers free before the next segment
 
     // Partial of split g for sequence b, slot g + b.
-    const int64_t slot = int64_t(g) + b;
+    const int64_t pslot = int64_t(g) + b;
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (head_ok) {
-      float* dst = a.part_o + ((slot * NB + j) * a.h + head) * G::kDL + sub * 128;
+      float* dst = a.part_o + ((pslot * NB + j) * a.h + head) * G::kDL + sub * 128;
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg)
 #pragma unroll
@@ -583,26 +626,28 @@ void decode_kernel(DecodeArgs a) {
           *reinterpret_cast<floatx4*>(dst + 32 * gg + 16 * hh + 4 * i) =
               floatx4{O[0][4 * gg + i], O[1][4 * gg + i], O[2][4 * gg + i], O[3][4 * gg + i]};
       if (hh == 0 && sub == 0) {
-        float* ml = a.part_ml + ((slot * NB + j) * a.h + head) * 2;
+        float* ml = a.part_ml + ((pslot * NB + j) * a.h + head) * 2;
         ml[0] = m_run;
         ml[1] = l_tot;
       }
     }
+    // The partial stores share the vector-memory counter with the next segment's tile loads.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 }
 
 // ------------------------------------------------------------------ combine kernel
 //
-// One workgroup per (query head i, 128-channel block q of the 512 latent channels,
-// group of up to 32 sequences). Block q lies in latent head j = q / (4/NB), channels
-// c0..c0+127 of it, c0 = (q % (4/NB)) * 128.
+// One workgroup per (query head i, block q of kCombBlock of the 512 latent channels, group of
+// up to 32 sequences). Block q lies in latent head j = q*kCombBlock / d_latent, channels
+// c0..c0+kCombBlock-1 of it, c0 = q*kCombBlock % d_latent.
 //  1. merge:   obar[b][k] = sum_s 2^{m_s-M} O_s[c0+k] / sum_s 2^{m_s-M} l_s over the splits
 //              s holding part of sequence b (slots g + b, g in [g_first, g_last]), into LDS.
 //  2. project: y_q[b][d] = sum_k obar[b][k] * W_UV[j][i][c0+k][d] on fp32 MFMA
-//              (M = sequences, N = 128 output channels, K = 128). Every W_UV row is read
-//              by exactly one workgroup of the grid.
-//  y_q goes to the workspace; finalize_kernel adds the four blocks in the fixed order
-//  q = 0..3 (the branch sum) and applies out_scale. (Summing inside this kernel would need
+//              (M = sequences, N = 128 output channels, K = kCombBlock). Every W_UV row is
+//              read by exactly one workgroup of the grid.
+//  y_q goes to the workspace; finalize_kernel adds the blocks in the fixed order q = 0, 1, ...
+//  (the branch sum) and applies out_scale. (Summing inside this kernel would need
 //  device-scope fences between workgroups on different L2 slices; their write-back and
 //  invalidate cost more than the extra launch.)
 
@@ -611,11 +656,13 @@ struct CombineArgs {
   const float* part_ml;
   const int64_t* prefix;
   const float* W_UV;
-  float* ypart;    // [groups][h][4][32][128]
+  float* ypart;    // [groups][h][kCombBlocks][32][128]
   int B, h;
 };
 
 constexpr int kCombSeqs = 32;
+constexpr int kCombBlocks = kLatentTotal / kCombBlock;
+constexpr int kCombTPS = kCombBlock / 16;  // merge threads per sequence, 4 channel quads each
 
 struct MergeState {
   float M, den;
@@ -640,11 +687,11 @@ __device__ __forceinline__ void merge_in(MergeState& st, float m, float l, const
 
 template <int NB>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  constexpr int WPB = 4 / NB;
   constexpr int DL = kLatentTotal / NB;
   constexpr int kBatch = 4;  // slots loaded together
-  __shared__ float ob[128][kCombSeqs];  // merged block, k-major: ob[k][b]
-  __shared__ float st_red[18 * 256];     // per (slot part, pair): M, den, acc[16] (only when parts > 1)
+  constexpr int kSteps = kCombBlock / 2;  // K steps of the 32x32x2 MFMA
+  __shared__ float ob[kCombBlock][kCombSeqs];  // merged block, k-major: ob[k][b]
+  __shared__ float st_red[18 * 256];            // per (slot part, pair): M, den, acc[16] (parts > 1)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -652,8 +699,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int i = blockIdx.x;
   const int q = blockIdx.y;
   const int grp = blockIdx.z;
-  const int j = q / WPB;
-  const int c0 = (q % WPB) * 128;
+  const int j = (q * kCombBlock) / DL;
+  const int c0 = (q * kCombBlock) % DL;
   const int b0 = grp * kCombSeqs;
   const int nb = min(kCombSeqs, a.B - b0);
   const int n = lane & 31, hh = lane >> 5;
@@ -661,23 +708,24 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   // The W_UV slice this wave multiplies by (rows c0 + 2kb + hh, column 32*wave + n), issued
   // first so that the loads overlap the merge.
   const float* wcol = a.W_UV + ((int64_t(j) * a.h + i) * DL + c0) * kDV + 32 * wave + n;
-  float wv[64];
+  float wv[kSteps];
 #pragma unroll
-  for (int kb = 0; kb < 64; ++kb) wv[kb] = wcol[(2 * kb + hh) * kDV];
+  for (int kb = 0; kb < kSteps; ++kb) wv[kb] = wcol[(2 * kb + hh) * kDV];
   __builtin_amdgcn_sched_barrier(0);
 
   const Plan plan{a.prefix[a.B + 1], int(a.prefix[a.B + 2])};
 
-  // ---- 1. merge. Eight threads per sequence, each owning channel quads cq0 + 8v (v < 4);
-  // with nbp = nb rounded up to a power of two, S = 32 / nbp slot parts share a sequence.
+  // ---- 1. merge. kCombTPS threads per sequence, each owning channel quads cq0 + kCombTPS*v
+  // (v < 4); with nbp = nb rounded up to a power of two, S = 256 / (nbp * kCombTPS) slot
+  // parts share a sequence.
   int nbp = 1;
   while (nbp < nb) nbp <<= 1;
-  const int NPP = nbp * 8;  // threads per slot part
+  const int NPP = nbp * kCombTPS;  // threads per slot part
   const int S = 256 / NPP;
   const int r = tid / NPP;
   const int rem = tid % NPP;
-  const int bl = rem / 8;
-  const int cq0 = rem % 8;
+  const int bl = rem / kCombTPS;
+  const int cq0 = rem % kCombTPS;
   const bool live = bl < nb;
   const int b = b0 + (live ? bl : 0);
 
@@ -700,7 +748,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
           ml[u] = *reinterpret_cast<const floatx2*>(a.part_ml + row * 2);
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            o[u][v] = *reinterpret_cast<const floatx4*>(a.part_o + row * DL + c0 + 4 * (cq0 + 8 * v));
+            o[u][v] = *reinterpret_cast<const floatx4*>(a.part_o + row * DL + c0 + 4 * (cq0 + kCombTPS * v));
           if (gg > gl) ml[u][0] = -INFINITY;  // past the end: re-read the last slot, then skip it
         }
 #pragma unroll
@@ -735,27 +783,27 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     const float inv = (live && st.den > 0.f) ? 1.f / st.den : 0.f;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const int k = 4 * (cq0 + 8 * v);
+      const int k = 4 * (cq0 + kCombTPS * v);
 #pragma unroll
       for (int e = 0; e < 4; ++e) ob[k + e][bl] = live ? st.acc[v][e] * inv : 0.f;
     }
   }
   // Sequences of the padded group beyond nbp read as zero.
-  for (int idx = tid; idx < 128 * kCombSeqs; idx += 256)
+  for (int idx = tid; idx < kCombBlock * kCombSeqs; idx += 256)
     if ((idx % kCombSeqs) >= nbp) ob[idx / kCombSeqs][idx % kCombSeqs] = 0.f;
   __syncthreads();
 
   // ---- 2. project: wave w computes output channels [32w, 32w+32) for all 32 sequences.
   floatx16 y = {};
 #pragma unroll
-  for (int kb = 0; kb < 64; ++kb) y = __builtin_amdgcn_mfma_f32_32x32x2f32(ob[2 * kb + hh][n], wv[kb], y, 0, 0, 0);
+  for (int kb = 0; kb < kSteps; ++kb) y = __builtin_amdgcn_mfma_f32_32x32x2f32(ob[2 * kb + hh][n], wv[kb], y, 0, 0, 0);
 
-  float* yq = a.ypart + ((int64_t(grp) * a.h + i) * 4 + q) * (kCombSeqs * kDV);
+  float* yq = a.ypart + ((int64_t(grp) * a.h + i) * kCombBlocks + q) * (kCombSeqs * kDV);
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) yq[(8 * (rr >> 2) + 4 * hh + (rr & 3)) * kDV + 32 * wave + n] = y[rr];
 }
 
-// out[b][i][:] = out_scale * (y_0 + y_1 + y_2 + y_3)[b][:], blocks added in this order.
+// out[b][i][:] = out_scale * (y_0 + y_1 + ...)[b][:], blocks added in this order.
 struct FinalizeArgs {
   const float* ypart;
   float* out;
@@ -772,10 +820,12 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
   const int i = int(bi % a.h);
   const int b = int(bi / a.h);
   const int grp = b / kCombSeqs, bl = b % kCombSeqs;
-  const floatx4* y = reinterpret_cast<const floatx4*>(a.ypart + ((int64_t(grp) * a.h + i) * 4) * (kCombSeqs * kDV) +
-                                                      bl * kDV) + d4;
+  const floatx4* y = reinterpret_cast<const floatx4*>(
+                         a.ypart + ((int64_t(grp) * a.h + i) * kCombBlocks) * (kCombSeqs * kDV) + bl * kDV) + d4;
   constexpr int kBlk = kCombSeqs * kDV / 4;
-  const floatx4 v = ((y[0] + y[kBlk]) + y[2 * kBlk]) + y[3 * kBlk];
+  floatx4 v = y[0];
+#pragma unroll
+  for (int qq = 1; qq < kCombBlocks; ++qq) v += y[qq * kBlk];
   reinterpret_cast<floatx4*>(a.out)[idx] = a.out_scale * v;
 }
 
@@ -1013,7 +1063,7 @@ extern "C" int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, fl
   c.ypart = reinterpret_cast<float*>(ws + lay.ypart_off);
   c.B = p->batch;
   c.h = p->num_heads;
-  const dim3 grid(p->num_heads, 4, (p->batch + kCombSeqs - 1) / kCombSeqs);
+  const dim3 grid(p->num_heads, kCombBlocks, (p->batch + kCombSeqs - 1) / kCombSeqs);
   hipLaunchKernelGGL(pick_combine(p->num_branches), grid, dim3(256), 0, static_cast<hipStream_t>(stream), c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");

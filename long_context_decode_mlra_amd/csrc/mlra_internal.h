@@ -14,13 +14,17 @@ constexpr int kHeadBlock = 32;            // query heads per MFMA column block
 constexpr int kLatentTotal = 512;         // NB * d_latent in every supported form
 constexpr int kDRope = 64;
 constexpr int kDV = 128;
+#ifndef MLRA_COMBINE_BLOCK
+#define MLRA_COMBINE_BLOCK 64
+#endif
+constexpr int kCombBlock = MLRA_COMBINE_BLOCK;  // latent channels per combine workgroup (64 or 128)
 
 // Workspace of one decode call:
 //   part_o  fp32 [slots][NB][h][d_latent]  unnormalised output of one split for one sequence
 //                                          (slot = split + sequence)
 //   part_ml fp32 [slots][NB][h][2]         (running max in log2 units, running sum)
 //   prefix  int64 [B + 3]                  first tile of each sequence, then T (total tiles), T, G
-//   ypart   fp32 [groups][h][4][32][d_v]   projected 128-channel blocks of up to 32 sequences
+//   ypart   fp32 [groups][h][512/kCombBlock][32][d_v]  projected channel blocks of up to 32 sequences
 // groups = ceil(B / 32).
 struct WorkspaceLayout {
   int64_t slots = 0;

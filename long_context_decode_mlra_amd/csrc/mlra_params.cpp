@@ -37,7 +37,8 @@ WorkspaceLayout workspace_layout(const mlra_decode_params& p, int32_t num_splits
   w.prefix_off = align256(w.part_ml_off + size_t(w.slots) * per_slot_ml);
   const size_t groups = (size_t(p.batch) + 31) / 32;
   w.ypart_off = align256(w.prefix_off + (size_t(p.batch) + 3) * sizeof(int64_t));
-  w.total = align256(w.ypart_off + groups * size_t(p.num_heads) * 4 * 32 * kDV * sizeof(float));
+  w.total = align256(w.ypart_off + groups * size_t(p.num_heads) * (kLatentTotal / kCombBlock) * 32 * kDV *
+                                       sizeof(float));
   return w;
 }
 

@@ -97,7 +97,7 @@ def test_workspace_size_with_explicit_splits_needs_no_device():
     expect = (slots * 32 * 512 * 4          # split partials of the output
               + slots * 4 * 32 * 2 * 4      # running max and sum per partial
               + (32 + 3) * 8                # tile prefix per sequence, T, G
-              + 1 * 32 * 4 * 32 * 128 * 4)  # projected 128-channel blocks, one group of 32 sequences
+              + 1 * 32 * 8 * 32 * 128 * 4)  # projected 64-channel blocks, one group of 32 sequences
     assert n.value >= expect and n.value % 256 == 0 and n.value < expect + 5 * 256
 
 
