@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of this "
                          "benchmark into the per-launch HBM traffic record under profiles/")
+    ap.add_argument("--absorb", action="store_true",
+                    help="also time the query-side absorption kernel (q_nope = W_UK q_pre) on this workload")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step recorded once as a HIP graph and replayed (reported beside)")
     return ap.parse_args()
@@ -223,6 +225,24 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
         graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    absorb = None
+    if args.absorb:
+        from mlra_workloads import make_absorption_inputs
+        q_pre, W_UK = make_absorption_inputs(w, seed=args.config, B=len(inp.seqlens))
+        q_pre, W_UK = q_pre.to(dev), W_UK.to(dev)
+        qn = torch.empty(len(inp.seqlens), w.h, w.NB, w.DL, dtype=w.torch_dtype, device=dev)
+        for _ in range(3):
+            mlra.absorb_query(q_pre, W_UK, qn)
+        ea = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ea[0].record(stream)
+        for _ in range(args.steps):
+            mlra.absorb_query(q_pre, W_UK, qn)
+        ea[1].record(stream)
+        torch.cuda.synchronize()
+        a_us = ea[0].elapsed_time(ea[1]) * 1e3 / args.steps
+        a_bytes = q_pre.numel() * q_pre.element_size() + W_UK.numel() * 4 + qn.numel() * qn.element_size()
+        absorb = {"us_per_call": round(a_us, 2), "algorithmic_bytes": a_bytes,
+                  "achieved_GBps": round(a_bytes / (a_us * 1e-6) / 1e9, 1)}
     dk = sorted(e[0].elapsed_time(e[1]) for e in evs)
     ck = sorted(e[1].elapsed_time(e[2]) for e in evs)
     dk_mean = sum(dk) / len(dk)
@@ -260,6 +280,7 @@ def main():
         "copy_probe_GBps": None if copy_gbps is None else round(copy_gbps, 1),
         "read_probe_GBps": None if read_gbps is None else round(read_gbps, 1),
         "roofline": roofline,
+        "absorb_query": absorb,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -145,6 +145,23 @@ int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, float* out, c
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Query-side absorption (decode step 1 of the pages; "Main Findings" bullet 4 and the
+ * block decomposition of "Key Contributions" #1): the NoPE key of query head i in latent
+ * head j is latent_j @ W_UK[j,i], so
+ *     q_nope[b,i,j,:] = W_UK[j,i] @ q_pre[b,i,j,:]      (d_latent x d_nope times d_nope)
+ * turns the NoPE query of each head into latent coordinates, the input mlra_decode takes.
+ *   q_pre   [B][h][NB] rows of d_nope = 128 elements (dtype), strides qpre_stride_b/h/j in
+ *           elements; qpre_stride_j = 0 shares one NoPE query across the latent heads
+ *   W_UK    fp32 [NB][h][d_latent][d_nope], contiguous (row = latent channel)
+ *   q_nope  output, dtype, laid out as mlra_decode reads it (p->q_stride_b, p->q_stride_h;
+ *           latent head j at offset j*d_latent); rounded to nearest (even) for bf16
+ * One kernel launch on `stream`. Returns 0 or a negative code.
+ */
+int mlra_absorb_query(const void* q_pre, const float* W_UK, void* q_nope, const mlra_decode_params* p,
+                      int32_t d_nope, int64_t qpre_stride_b, int64_t qpre_stride_h, int64_t qpre_stride_j,
+                      void* stream);
+
+/*
  * The split plan the two kernels follow, written out for inspection. Every
  * sequence is cut into tiles of MLRA_TILE_TOKENS tokens; the T tiles of all
  * sequences, in order, are cut into G = min(num_splits, T) contiguous ranges

@@ -18,7 +18,7 @@ ERRORS = {0: "MLRA_OK", -1: "MLRA_ERR_NULL", -2: "MLRA_ERR_SHAPE", -3: "MLRA_ERR
 # Every symbol include/mlra.h declares.
 EXPORTS = ("mlra_abi_version", "mlra_last_error", "mlra_check_params", "mlra_decode_num_splits",
            "mlra_decode_workspace_size", "mlra_decode", "mlra_decode_splitkv", "mlra_decode_combine",
-           "mlra_decode_plan", "mlra_copy_bandwidth_probe", "mlra_read_bandwidth_probe")
+           "mlra_decode_plan", "mlra_copy_bandwidth_probe", "mlra_read_bandwidth_probe", "mlra_absorb_query")
 
 
 class DecodeParams(ctypes.Structure):
@@ -64,6 +64,8 @@ def lib() -> ctypes.CDLL:
     L.mlra_decode_plan.argtypes = [vp, i32, i32, i32, vp, vp]
     L.mlra_copy_bandwidth_probe.argtypes = [vp, vp, sz, vp]
     L.mlra_read_bandwidth_probe.argtypes = [vp, sz, vp, vp]
+    i64 = ctypes.c_int64
+    L.mlra_absorb_query.argtypes = [vp, vp, vp, P, i32, i64, i64, i64, vp]
     for name in EXPORTS:
         if name not in ("mlra_last_error", "mlra_abi_version"):
             getattr(L, name).restype = ctypes.c_int

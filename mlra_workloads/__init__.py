@@ -25,7 +25,7 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["Workload", "CONFIGS", "make_inputs", "DecodeInputs", "draw_lengths"]
+__all__ = ["Workload", "CONFIGS", "make_inputs", "DecodeInputs", "draw_lengths", "make_absorption_inputs"]
 
 D_ROPE = 64
 D_V = 128
@@ -255,3 +255,22 @@ def make_inputs(w: Workload, seed: int, *, lengths: Optional[Sequence[int]] = No
     return DecodeInputs(w=w, seqlens=seqlens, max_seqlen=msl, q_nope=q_nope, q_rope=q_rope,
                         latent=latent, rope=rope, W_UV=W_UV, block_table=block_table,
                         max_pages=max_pages, q_joint=q_joint, cache_joint=cache_joint)
+
+
+D_NOPE = 128
+
+
+def make_absorption_inputs(w: Workload, seed: int, B: int, *, shared_query: bool = False):
+    """Pre-absorption NoPE queries and key up-projections for the query-side absorption step.
+
+    From their own generator (seed 1000 * seed + 17), so the workload's other draws are
+    unchanged: q_pre [B, h, NB, 128] N(0, 1) in the workload dtype (one vector per head shared
+    by every latent head when shared_query: returned as a stride-0 view), then W_UK
+    [NB, h, d_latent, 128] fp32 N(0, 1/128)."""
+    gen = torch.Generator().manual_seed(1000 * int(seed) + 17)
+    if shared_query:
+        q = _randn(gen, (B, w.h, 1, D_NOPE), 1.0, w.torch_dtype).expand(B, w.h, w.NB, D_NOPE)
+    else:
+        q = _randn(gen, (B, w.h, w.NB, D_NOPE), 1.0, w.torch_dtype)
+    W_UK = _randn(gen, (w.NB, w.h, w.DL, D_NOPE), 1.0 / math.sqrt(D_NOPE), torch.float32)
+    return q, W_UK

@@ -51,6 +51,7 @@ except Exception:  # pragma: no cover
 __all__ = [
     "as_f64", "physical_rows", "rope_scores", "branch_scores", "softmax_average",
     "up_project", "branch_sum", "decode", "decode_split", "decode_inputs", "partial_stats", "merge_partials",
+    "absorb",
 ]
 
 
@@ -189,6 +190,14 @@ def decode_split(q_nope, q_rope, latent, rope, W_UV, seqlens, *, sm_scale: float
             projected.append(up_project(merge_partials(parts), W[j]))
         out[b] = branch_sum(projected, out_scale)
     return out
+
+
+def absorb(q_pre, W_UK) -> np.ndarray:
+    """Query-side absorption ("Main Findings" bullet 4; block decomposition, "Key
+    Contributions" #1): the NoPE key of query head i in latent head j is C_j @ W_UK[j,i]
+    (W_UK[j,i] is d_latent x d_nope), so <q_pre, C_j @ W_UK[j,i]> = <W_UK[j,i] @ q_pre, C_j>.
+    q_pre [B, h, NB, d_nope], W_UK [NB, h, d_latent, d_nope] -> q_nope [B, h, NB, d_latent]."""
+    return np.einsum("jicn,bijn->bijc", as_f64(W_UK), as_f64(q_pre))
 
 
 def decode_inputs(inp, batch_indices: Optional[Sequence[int]] = None, **overrides) -> np.ndarray:

@@ -284,6 +284,36 @@ def pin_empty_sequence(decode):
     assert np.all(np.isfinite(got[1])) and np.any(got[1] != 0)
 
 
+def pin_absorb_is_unabsorbed_attention(decode, absorb=None):
+    """decode(absorb(q_pre, W_UK)) equals attention with the per-head NoPE keys C_j @ W_UK[j,i]
+    materialised and dotted with q_pre directly (no absorption anywhere on this side)."""
+    import oracle
+    absorb = absorb or oracle.absorb
+    rng = np.random.default_rng(21)
+    for NB in (4, 1):
+        B, h, DL, DR, DV, dn, Ls = 2, 3, 4 if NB == 4 else 8, 2, 3, 5, (6, 3)
+        msl = max(Ls)
+        q_pre = rng.standard_normal((B, h, NB, dn))
+        W_UK = rng.standard_normal((NB, h, DL, dn))
+        q_rope = rng.standard_normal((B, h, DR))
+        lat = rng.standard_normal((B * msl, NB, DL))
+        rope = rng.standard_normal((B * msl, DR))
+        W_UV = rng.standard_normal((NB, h, DL, DV))
+        got = decode(absorb(q_pre, W_UK), q_rope, lat, rope, W_UV, list(Ls), sm_scale=0.3,
+                     out_scale=1 / math.sqrt(NB), max_seqlen=msl)
+        for b in range(B):
+            rows = np.arange(b * msl, b * msl + Ls[b])
+            for i in range(h):
+                acc = np.zeros(DV)
+                for j in range(NB):
+                    K = lat[rows, j, :] @ W_UK[j, i]                    # [L, dn] NoPE keys
+                    logit = 0.3 * (K @ q_pre[b, i, j] + rope[rows] @ q_rope[b, i])
+                    p = np.exp(logit - logit.max())
+                    p /= p.sum()
+                    acc += (p @ lat[rows, j, :]) @ W_UV[j, i]           # values then up-projection
+                np.testing.assert_allclose(got[b, i], acc / math.sqrt(NB), rtol=1e-11, atol=1e-12)
+
+
 ALL_PINS = [pin_golden, pin_unabsorbed_bruteforce, pin_sdpa_library, pin_shared_rope_half_mla,
             pin_branches_separate, pin_one_token, pin_uniform, pin_paged_equals_contiguous,
-            pin_token_permutation, pin_shift_and_range, pin_empty_sequence]
+            pin_token_permutation, pin_shift_and_range, pin_empty_sequence, pin_absorb_is_unabsorbed_attention]

@@ -241,3 +241,34 @@ def test_graph_replay_matches_eager():
         junk = torch.randn(1 << 16, device="cuda").sum()  # eager work between replays
         torch.cuda.synchronize()
     assert_parity(eager.cpu().double().numpy(), oracle.decode_inputs(inp), label="graph")
+
+
+# ----------------------------------------------------------------- query-side absorption (decode step 1)
+from mlra_workloads import make_absorption_inputs
+
+
+@pytest.mark.parametrize("cfg,shared", [(2, False), (2, True), (4, False), (1, False)])
+def test_absorb_query_then_decode(cfg, shared):
+    """GPU absorption q_nope = W_UK q_pre against the oracle's, then the full three-step decode
+    (absorb on the GPU, attend, up-project) against the oracle on the fp64 absorbed query."""
+    mlra = _mlra()
+    w = CONFIGS[cfg].replace(B=3, lengths=("list", (257, 1, 90)))
+    inp = make_inputs(w, seed=cfg, max_seqlen=288)
+    q_pre, W_UK = make_absorption_inputs(w, seed=cfg, B=3, shared_query=shared)
+    d = inp.to("cuda")
+    q_pre_d = q_pre.to("cuda") if not shared else q_pre[:, :, :1].to("cuda").expand_as(q_pre)
+    q_nope = torch.empty(3, w.h, w.NB, w.DL, dtype=w.torch_dtype, device="cuda")
+    mlra.absorb_query(q_pre_d, W_UK.to("cuda"), q_nope)
+    torch.cuda.synchronize()
+    ref_q = oracle.absorb(q_pre, W_UK)
+    got_q = q_nope.cpu().double().numpy()
+    # bf16 output: one rounding to nearest (relative 2^-9) of an fp32-accumulated dot product.
+    bound = (2.0 ** -8 if w.dtype == "bf16" else 1e-5) * np.abs(ref_q) + 1e-5
+    assert np.all(np.abs(got_q - ref_q) <= bound), float(np.max(np.abs(got_q - ref_q) - bound))
+    out = mlra.decode(q_nope, d.q_rope, d.latent, d.rope, d.seqlens, d.W_UV, sm_scale=w.sm_scale,
+                      out_scale=w.gamma, max_seqlen=inp.max_seqlen)
+    torch.cuda.synchronize()
+    ref = oracle.decode(ref_q, inp.q_rope, inp.latent, inp.rope, inp.W_UV, inp.seqlens, sm_scale=w.sm_scale,
+                        out_scale=w.gamma, max_seqlen=inp.max_seqlen)
+    tol = dict(rel_l2=1e-4, max_abs=1e-3) if w.dtype == "f32" else {}
+    assert_parity(out.cpu().double().numpy(), ref, label=f"absorb+decode cfg{cfg} shared={shared}", **tol)

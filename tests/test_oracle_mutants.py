@@ -182,3 +182,14 @@ def test_split_merge_mutant_is_caught(monkeypatch):
     a = oracle.decode(c["q_nope"], c["q_rope"], c["latent"], c["rope"], c["W_UV"], c["seqlens"], **kw)
     s = M.decode_split(c["q_nope"], c["q_rope"], c["latent"], c["rope"], c["W_UV"], c["seqlens"], chunk=4, **kw)
     assert not np.allclose(a, s, rtol=1e-6)
+
+
+def test_absorb_mutants_are_caught():
+    """W_UK of head 0 used for every head, or the query of the wrong latent head, breaks the
+    absorption pin."""
+    import oracle_pins as P
+    bad_head = lambda q_pre, W_UK: np.einsum("jcn,bijn->bijc", np.asarray(W_UK)[:, 0], q_pre)
+    bad_branch = lambda q_pre, W_UK: np.einsum("jicn,bijn->bijc", W_UK, np.roll(q_pre, 1, axis=2))
+    for bad in (bad_head, bad_branch):
+        with pytest.raises(AssertionError):
+            P.pin_absorb_is_unabsorbed_attention(oracle.decode, bad)
