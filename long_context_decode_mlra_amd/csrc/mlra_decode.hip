@@ -636,6 +636,184 @@ void decode_kernel(DecodeArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ split-head decode (NB = 1, 2; bf16)
+//
+// For one or two latent heads of 512 or 256 channels, splitting the logit channels across
+// waves would need the partial logits summed between waves every tile. Instead each wave
+// (cp, hq) takes 16 query heads hq and computes their full logits itself (latent head
+// j = cp for NB = 2; all 512 channels for NB = 1, where the two waves of a head group
+// compute the same logits), then accumulates PV for latent channels [256*cp, 256*cp + 256).
+// No cross-wave exchange is left, so tiles go straight into LDS as in decode_kernel.
+// MFMA 16x16x32 bf16, tokens as M (two blocks of 16), heads as N, 32 channels as K:
+// lane (n16, g) holds head 16*hq + n16 and tokens 16*mb + 4*g + r (mb < 2, r < 4).
+
+template <int NB, int HB>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, 256 * HB), amdgpu_waves_per_eu(2, 2)))
+void decode_hs_kernel(DecodeArgs a) {
+  static_assert(NB == 1 || NB == 2, "split-head decode is for one or two latent heads");
+  using G = Geo<__bf16, NB, HB>;
+  constexpr int kLatSteps = NB == 1 ? 16 : 8;  // 32-channel K steps over the latent part of the logit
+  constexpr int kSteps = kLatSteps + 2;        // plus the 64 RoPE channels
+  constexpr int DL = kLatentTotal / NB;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * G::kTileBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cp = wave & 1;   // PV channels [256*cp, 256*cp + 256)
+  const int hq = wave >> 1;  // query heads [16*hq, 16*hq + 16)
+  const int j = NB == 2 ? cp : 0;
+  const int qk_c0 = NB == 2 ? 256 * cp : 0;  // first latent channel of this wave's logits
+  const int n16 = lane & 15;
+  const int g = lane >> 4;
+  const int head = 16 * hq + n16;
+  const bool head_ok = head < a.h;
+
+  const Plan plan = make_plan(a.seqlens, a.B, a.G_req);
+  const int gsplit = blockIdx.x;
+  if (gsplit == 0 && wave == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
+  if (gsplit >= plan.G) return;
+  SegmentWalk walk = begin_walk(a.seqlens, a.B, gsplit, plan);
+
+  int b, ta, te;
+  while (next_segment(a.seqlens, a.B, walk, b, ta, te)) {
+    b = __builtin_amdgcn_readfirstlane(b);
+    ta = __builtin_amdgcn_readfirstlane(ta);
+    te = __builtin_amdgcn_readfirstlane(te);
+    const int L = scalar_read(a.seqlens + b);
+
+    // Query operands: K step st covers channels qk_c0 + 32*st + 8*g .. +8 (latent), then RoPE.
+    bf16x8 qv[kSteps];
+    {
+      const unsigned char* qn = a.q_nope + int64_t(b) * a.q_sb + int64_t(head) * a.q_sh;
+      const unsigned char* qr = a.q_rope + int64_t(b) * a.qr_sb + int64_t(head) * a.qr_sh;
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        const unsigned char* src = st < kLatSteps ? qn + (qk_c0 + 32 * st + 8 * g) * 2 : qr + (32 * (st - kLatSteps) + 8 * g) * 2;
+        qv[st] = head_ok ? *reinterpret_cast<const bf16x8*>(src) : bf16x8{};
+      }
+    }
+    floatx4 O[16] = {};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    issue_tile_dma<__bf16, NB, HB>(a, b, L, ta, wave, lane, smem);
+    for (int k = ta; k < te; ++k) {
+      unsigned char* buf = smem + ((k - ta) & 1) * G::kTileBytes;
+      unsigned char* idle = smem + (((k - ta) & 1) ^ 1) * G::kTileBytes;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile k has landed
+      lds_barrier();  // every wave's part landed; every wave is done with tile k-1's buffer
+      if (k + 1 < te) issue_tile_dma<__bf16, NB, HB>(a, b, L, k + 1, wave, lane, idle);
+
+      // S^T for tokens 16*mb + n16 (A rows) and this wave's 16 heads.
+      floatx4 s2[2] = {};
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int t = 16 * mb + n16;
+        const unsigned char* row = buf + t * G::kLatRow;
+        const unsigned char* rrow = buf + G::kLatTile + t * G::kRopeRow;
+        const int sw = t & 7;
+#pragma unroll
+        for (int st = 0; st < kSteps; ++st) {
+          bf16x8 kk;
+          if (st < kLatSteps)
+            kk = *reinterpret_cast<const bf16x8*>(row + ((((qk_c0 >> 3) + 4 * st + g) ^ sw) << 4));
+          else
+            kk = *reinterpret_cast<const bf16x8*>(rrow + (((4 * (st - kLatSteps) + g) ^ sw) << 4));
+          s2[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qv[st], s2[mb], 0, 0, 0);
+        }
+      }
+      float sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = s2[e >> 2][e & 3];  // token 16*(e>>2) + 4*g + (e&3)
+      const int n_valid = L - k * kTile;
+      if (n_valid < kTile) {
+        const int lim = n_valid - 4 * g;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (16 * (e >> 2) + (e & 3) >= lim) sv[e] = -INFINITY;
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mt = mx * a.c;
+      const bool raise = mt > m_run + kRescaleSlack;
+      if (__ballot(raise)) {
+        const float mnew = raise ? mt : m_run;
+        const float alpha = (mnew == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
+        l_run *= alpha;
+#pragma unroll
+        for (int o = 0; o < 16; ++o) O[o] *= alpha;
+        m_run = mnew;
+      }
+      float psum = 0.f;
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[e], a.c, -m_run));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[e + 1], a.c, -m_run));
+        psum += p0 + p1;
+        const bf16x2 v = __builtin_convertvector((floatx2{p0, p1}), bf16x2);
+        pb[e] = v[0];
+        pb[e + 1] = v[1];
+      }
+      l_run += psum;
+
+      // O^T[channel][head] += V^T P^T. K index 8*g + e is token 16*(e>>2) + 4*g + (e&3), whose
+      // row has tau & 7 = 4*(g&1) + (e&3). M-block 4*blk + q holds channel
+      // 256*cp + 64*blk + 4*m + q in row m = n16.
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const int chunk = ((256 * cp + 64 * blk) >> 3) + (n16 >> 1);
+        u32x2 d[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tau = 16 * (e >> 2) + 4 * g + (e & 3);
+          d[e] = *reinterpret_cast<const u32x2*>(buf + tau * G::kLatRow + ((chunk ^ (4 * (g & 1) + (e & 3))) << 4) +
+                                                 ((n16 & 1) << 3));
+        }
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const uint32_t sel = (qq & 1) ? 0x07060302u : 0x05040100u;
+          u32x4 av;
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const uint32_t lo = (qq < 2) ? d[2 * pp][0] : d[2 * pp][1];
+            const uint32_t hi = (qq < 2) ? d[2 * pp + 1][0] : d[2 * pp + 1][1];
+            av[pp] = __builtin_amdgcn_perm(hi, lo, sel);
+          }
+          O[4 * blk + qq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb,
+                                                                    O[4 * blk + qq], 0, 0, 0);
+        }
+      }
+    }
+    lds_barrier();  // both tile buffers free before the next segment
+
+    // Partial of split gsplit for sequence b, slot gsplit + b. Lane (n16, g) holds channels
+    // 256*cp + 64*blk + 16*g + 4*r + qq in O[4*blk + qq][r].
+    const int64_t pslot = int64_t(gsplit) + b;
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (head_ok) {
+      float* dst = a.part_o + ((pslot * NB + j) * a.h + head) * DL + (NB == 1 ? 256 * cp : 0);
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<floatx4*>(dst + 64 * blk + 16 * g + 4 * r) =
+              floatx4{O[4 * blk][r], O[4 * blk + 1][r], O[4 * blk + 2][r], O[4 * blk + 3][r]};
+      if (g == 0 && (NB == 2 || cp == 0)) {
+        float* ml = a.part_ml + ((pslot * NB + j) * a.h + head) * 2;
+        ml[0] = m_run;
+        ml[1] = l_tot;
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
 // ------------------------------------------------------------------ combine kernel
 //
 // One workgroup per (query head i, block q of kCombBlock of the 512 latent channels, group of
@@ -963,8 +1141,8 @@ DecodeFn pick_decode(int dtype, int nb, int hb) {
   if (nb == NB_) return hb == 1 ? decode_kernel<T, NB_, 1> : decode_kernel<T, NB_, 2>;
   if (dtype == MLRA_BF16) {
     MLRA_PICK(__bf16, 4)
-    MLRA_PICK(__bf16, 2)
-    MLRA_PICK(__bf16, 1)
+    if (nb == 2) return hb == 1 ? decode_hs_kernel<2, 1> : decode_hs_kernel<2, 2>;
+    if (nb == 1) return hb == 1 ? decode_hs_kernel<1, 1> : decode_hs_kernel<1, 2>;
   } else {
     MLRA_PICK(float, 4)
     MLRA_PICK(float, 2)
