@@ -224,10 +224,18 @@ struct DecodeArgs {
   float c;                           // sm_scale * log2(e)
 };
 
-// Tile geometry. The LDS copy of a tile keeps the cache row order; within each
-// row the 16-byte chunk c of token t sits at chunk position c ^ (t & 7), so the
-// MFMA operand reads (32 tokens at one chunk, or 8-byte column groups of one
-// token) hit distinct banks.
+// Tile geometry. The LDS copy of a tile keeps the cache row order; within each row the
+// 16-byte chunk c of token t sits at chunk position c ^ lat_swizzle(t) (latent rows) or
+// c ^ rope_swizzle(t) (RoPE rows), so the MFMA operand reads hit distinct banks: 16
+// consecutive rows read at one logical chunk land on 16 different 16-byte bank groups
+// (latent rows are 1 KiB or 2 KiB apart: only the chunk position picks the banks), rows
+// 4 apart read as 8-byte column groups land in different 128-byte halves, and two 128-byte
+// bf16 RoPE rows that share a 256-byte bank span never collide.
+__device__ __forceinline__ int lat_swizzle(int t) { return (t & 7) | ((((t >> 3) ^ (t >> 2)) & 1) << 3); }
+template <int kRopeRowBytes>
+__device__ __forceinline__ int rope_swizzle(int t) {
+  return kRopeRowBytes == 128 ? ((t >> 1) & 7) : (t & 15);
+}
 template <typename T, int NB, int HB>
 struct Geo {
   static constexpr int kEsz = int(sizeof(T));
@@ -333,12 +341,12 @@ __device__ __forceinline__ const unsigned char* load_src(const DecodeArgs& a, co
   // Offsets inside one tile fit 32 bits: 32 rows times a stride below 2^25 bytes.
   if (off < G::kLatTile) {
     const int t = off / G::kLatRow;
-    const int c = ((off % G::kLatRow) >> 4) ^ (t & 7);
+    const int c = ((off % G::kLatRow) >> 4) ^ lat_swizzle(t);
     return tr.lat + (min(t, tr.last) * int(a.lat_stride) + c * 16);
   }
   const int o2 = off - G::kLatTile;
   const int t = o2 / G::kRopeRow;
-  const int c = ((o2 % G::kRopeRow) >> 4) ^ (t & 7);
+  const int c = ((o2 % G::kRopeRow) >> 4) ^ rope_swizzle<G::kRopeRow>(t);
   return tr.rope + (min(t, tr.last) * int(a.rope_stride) + c * 16);
 }
 
@@ -395,34 +403,32 @@ __device__ __forceinline__ floatx16 tile_logits(const unsigned char* buf, int wq
   floatx16 s = {};
   const unsigned char* row = buf + n * G::kLatRow;
   const unsigned char* rrow = buf + G::kLatTile + n * G::kRopeRow;
-  const int sw = n & 7;
+  const int sw = lat_swizzle(n);
+  const int rsw = rope_swizzle<G::kRopeRow>(n);
   const int sub = wq % G::kWPB;
   if constexpr (sizeof(T) == 2) {
-    // Chunk 16*wq + 2*ks + hh of row n sits at ((2*(ks&3) + hh) ^ sw) + 8*(ks>>2) + 16*wq:
-    // four lane-dependent bases, the rest are immediate offsets.
-    const unsigned char* base = row + (wq << 8);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const bf16x8 k = *reinterpret_cast<const bf16x8*>(base + (((2 * (ks & 3) + hh) ^ sw) << 4) + ((ks >> 2) << 7));
+      const bf16x8 k = *reinterpret_cast<const bf16x8*>(row + ((16 * wq + ((2 * ks + hh) ^ sw)) << 4));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, q.lat[ks], s, 0, 0, 0);
     }
 #pragma unroll
     for (int rs = 0; rs < QOps<T, NB>::kRopeSteps; ++rs) {
       const int ks = sub * QOps<T, NB>::kRopeSteps + rs;
-      const bf16x8 k = *reinterpret_cast<const bf16x8*>(rrow + (((2 * ks + hh) ^ sw) << 4));
+      const bf16x8 k = *reinterpret_cast<const bf16x8*>(rrow + (((2 * ks + hh) ^ rsw) << 4));
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k, q.rope[rs], s, 0, 0, 0);
     }
   } else {
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
-      const floatx4 k = *reinterpret_cast<const floatx4*>(row + (((32 * wq + 2 * g + hh) ^ sw) << 4));
+      const floatx4 k = *reinterpret_cast<const floatx4*>(row + ((32 * wq + ((2 * g + hh) ^ sw)) << 4));
 #pragma unroll
       for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(k[e], q.lat[g][e], s, 0, 0, 0);
     }
 #pragma unroll
     for (int rg = 0; rg < QOps<T, NB>::kRopeGroups; ++rg) {
       const int g = sub * QOps<T, NB>::kRopeGroups + rg;
-      const floatx4 k = *reinterpret_cast<const floatx4*>(rrow + (((2 * g + hh) ^ sw) << 4));
+      const floatx4 k = *reinterpret_cast<const floatx4*>(rrow + (((2 * g + hh) ^ rsw) << 4));
 #pragma unroll
       for (int e = 0; e < 4; ++e) s = __builtin_amdgcn_mfma_f32_32x32x2f32(k[e], q.rope[rg][e], s, 0, 0, 0);
     }
@@ -438,12 +444,14 @@ __device__ __forceinline__ void tile_pv(const unsigned char* buf, int wq, int n,
                                         floatx16 (&O)[4]) {
   using G = Geo<T, NB, HB>;
   if constexpr (sizeof(T) == 2) {
-    // Token tau = 16*ks + 8*(e>>2) + 4*hh + (e&3) has tau & 7 = 4*hh + (e&3): four
-    // lane-dependent bases (one per e&3); the token's row offset is an immediate.
-    const unsigned char* vb[4];
+    // Token tau = 16*ks + 8*(e>>2) + 4*hh + (e&3): its swizzle depends on e and hh only, so
+    // there is one lane-dependent base per e and the ks part of the row is an immediate.
+    const unsigned char* vb[8];
 #pragma unroll
-    for (int e3 = 0; e3 < 4; ++e3)
-      vb[e3] = buf + (4 * hh + e3) * G::kLatRow + (((16 * wq + (n >> 1)) ^ (4 * hh + e3)) << 4) + ((n & 1) << 3);
+    for (int e = 0; e < 8; ++e) {
+      const int t0 = 8 * (e >> 2) + 4 * hh + (e & 3);
+      vb[e] = buf + t0 * G::kLatRow + (((16 * wq + (n >> 1)) ^ lat_swizzle(t0)) << 4) + ((n & 1) << 3);
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       bf16x8 pb;
@@ -457,7 +465,7 @@ __device__ __forceinline__ void tile_pv(const unsigned char* buf, int wq, int n,
       u32x2 d[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        d[e] = *reinterpret_cast<const u32x2*>(vb[e & 3] + (16 * ks + 8 * (e >> 2)) * G::kLatRow);
+        d[e] = *reinterpret_cast<const u32x2*>(vb[e] + 16 * ks * G::kLatRow);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         const uint32_t sel = (mb & 1) ? 0x07060302u : 0x05040100u;
@@ -472,14 +480,12 @@ __device__ __forceinline__ void tile_pv(const unsigned char* buf, int wq, int n,
       }
     }
   } else {
-    // Token tau = 8*(r>>2) + 4*hh + (r&3): tau & 7 = 4*hh + (r&3).
-    const unsigned char* vb[4];
-#pragma unroll
-    for (int r3 = 0; r3 < 4; ++r3)
-      vb[r3] = buf + (4 * hh + r3) * G::kLatRow + (((32 * wq + n) ^ (4 * hh + r3)) << 4);
+    // Token tau = 8*(r>>2) + 4*hh + (r&3); lat_swizzle(tau) repeats with period 16 in tau.
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const floatx4 v = *reinterpret_cast<const floatx4*>(vb[r & 3] + 8 * (r >> 2) * G::kLatRow);
+      const int tau = 8 * (r >> 2) + 4 * hh + (r & 3);
+      const floatx4 v =
+          *reinterpret_cast<const floatx4*>(buf + tau * G::kLatRow + (((32 * wq + n) ^ lat_swizzle(tau)) << 4));
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) O[mb] = __builtin_amdgcn_mfma_f32_32x32x2f32(v[mb], p[r], O[mb], 0, 0, 0);
     }
@@ -638,12 +644,13 @@ void decode_kernel(DecodeArgs a) {
 
 // ------------------------------------------------------------------ split-head decode (NB = 1, 2; bf16)
 //
-// For one or two latent heads of 512 or 256 channels, splitting the logit channels across
-// waves would need the partial logits summed between waves every tile. Instead each wave
-// (cp, hq) takes 16 query heads hq and computes their full logits itself (latent head
-// j = cp for NB = 2; all 512 channels for NB = 1, where the two waves of a head group
-// compute the same logits), then accumulates PV for latent channels [256*cp, 256*cp + 256).
-// No cross-wave exchange is left, so tiles go straight into LDS as in decode_kernel.
+// For one or two latent heads of 512 or 256 channels, splitting the logit channels over all
+// four waves would need every wave's partial logits summed each tile. Instead each wave
+// (cp, hq) takes 16 query heads hq and accumulates PV for latent channels [256*cp, +256).
+// NB = 2: that is latent head j = cp, and the wave computes its full logits (256 latent +
+// 64 RoPE channels) itself. NB = 1: the two waves of a head group each compute half of the
+// 576-channel logit (256 latent + 32 RoPE channels) and add the other half from a small LDS
+// exchange, in a fixed order so both hold identical logits. Tiles go straight into LDS.
 // MFMA 16x16x32 bf16, tokens as M (two blocks of 16), heads as N, 32 channels as K:
 // lane (n16, g) holds head 16*hq + n16 and tokens 16*mb + 4*g + r (mb < 2, r < 4).
 
@@ -652,18 +659,22 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, 256 * HB), amdgpu_waves
 void decode_hs_kernel(DecodeArgs a) {
   static_assert(NB == 1 || NB == 2, "split-head decode is for one or two latent heads");
   using G = Geo<__bf16, NB, HB>;
-  constexpr int kLatSteps = NB == 1 ? 16 : 8;  // 32-channel K steps over the latent part of the logit
-  constexpr int kSteps = kLatSteps + 2;        // plus the 64 RoPE channels
+  constexpr int kLatSteps = 8;                   // 32-channel K steps over 256 latent channels
+  constexpr int kRopeSteps = NB == 2 ? 2 : 1;    // over 64 or 32 RoPE channels
+  constexpr int kSteps = kLatSteps + kRopeSteps;
   constexpr int DL = kLatentTotal / NB;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * G::kTileBytes];
+  constexpr int kXchBytes = NB == 1 ? 4 * HB * 2 * 64 * 16 : 0;  // per wave: 2 M-blocks x 64 lanes x 16 B
+  // Two waves per SIMD: two workgroups per compute unit of one head block, one of two.
+  static_assert(2 * G::kTileBytes + kXchBytes <= 81920 * HB, "LDS for two waves per SIMD");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * G::kTileBytes + kXchBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cp = wave & 1;   // PV channels [256*cp, 256*cp + 256)
+  const int cp = wave & 1;   // PV channels [256*cp, 256*cp + 256); logit channels, see above
   const int hq = wave >> 1;  // query heads [16*hq, 16*hq + 16)
   const int j = NB == 2 ? cp : 0;
-  const int qk_c0 = NB == 2 ? 256 * cp : 0;  // first latent channel of this wave's logits
+  const int qk_c0 = 256 * cp;  // first latent channel of this wave's logit K steps
   const int n16 = lane & 15;
   const int g = lane >> 4;
   const int head = 16 * hq + n16;
@@ -682,14 +693,16 @@ void decode_hs_kernel(DecodeArgs a) {
     te = __builtin_amdgcn_readfirstlane(te);
     const int L = scalar_read(a.seqlens + b);
 
-    // Query operands: K step st covers channels qk_c0 + 32*st + 8*g .. +8 (latent), then RoPE.
+    // Query operands: K step st < 8 covers latent channels qk_c0 + 32*st + 8*g .. +8; the RoPE
+    // steps cover RoPE channels 32*rs + 8*g (NB = 2: rs = 0, 1; NB = 1: rs = cp).
     bf16x8 qv[kSteps];
     {
       const unsigned char* qn = a.q_nope + int64_t(b) * a.q_sb + int64_t(head) * a.q_sh;
       const unsigned char* qr = a.q_rope + int64_t(b) * a.qr_sb + int64_t(head) * a.qr_sh;
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
-        const unsigned char* src = st < kLatSteps ? qn + (qk_c0 + 32 * st + 8 * g) * 2 : qr + (32 * (st - kLatSteps) + 8 * g) * 2;
+        const int rs = NB == 2 ? st - kLatSteps : cp;
+        const unsigned char* src = st < kLatSteps ? qn + (qk_c0 + 32 * st + 8 * g) * 2 : qr + (32 * rs + 8 * g) * 2;
         qv[st] = head_ok ? *reinterpret_cast<const bf16x8*>(src) : bf16x8{};
       }
     }
@@ -706,22 +719,43 @@ void decode_hs_kernel(DecodeArgs a) {
       if (k + 1 < te) issue_tile_dma<__bf16, NB, HB>(a, b, L, k + 1, wave, lane, idle);
 
       // S^T for tokens 16*mb + n16 (A rows) and this wave's 16 heads.
+      // K step st = 4u + v reads chunk qk_c0/8 + 16u + ((4v + g) ^ sw) of row 16*mb + n16: the
+      // swizzle only permutes the low four bits, so four lane-dependent bases (one per v) and
+      // immediate offsets cover every step; the swizzle of both rows is lat_swizzle(n16).
       floatx4 s2[2] = {};
+      const int sw = lat_swizzle(n16);
+      const int rsw = rope_swizzle<G::kRopeRow>(n16);
+      const unsigned char* kb[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) kb[v] = buf + n16 * G::kLatRow + qk_c0 * 2 + (((4 * v + g) ^ sw) << 4);
+      const unsigned char* rb[kRopeSteps];
+#pragma unroll
+      for (int v = 0; v < kRopeSteps; ++v) {
+        const int rs = NB == 2 ? v : cp;
+        rb[v] = buf + G::kLatTile + n16 * G::kRopeRow + (((4 * rs + g) ^ rsw) << 4);
+      }
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const int t = 16 * mb + n16;
-        const unsigned char* row = buf + t * G::kLatRow;
-        const unsigned char* rrow = buf + G::kLatTile + t * G::kRopeRow;
-        const int sw = t & 7;
 #pragma unroll
         for (int st = 0; st < kSteps; ++st) {
           bf16x8 kk;
           if (st < kLatSteps)
-            kk = *reinterpret_cast<const bf16x8*>(row + ((((qk_c0 >> 3) + 4 * st + g) ^ sw) << 4));
+            kk = *reinterpret_cast<const bf16x8*>(kb[st & 3] + 16 * mb * G::kLatRow + (st >> 2) * 256);
           else
-            kk = *reinterpret_cast<const bf16x8*>(rrow + (((4 * (st - kLatSteps) + g) ^ sw) << 4));
+            kk = *reinterpret_cast<const bf16x8*>(rb[st - kLatSteps] + 16 * mb * G::kRopeRow);
           s2[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qv[st], s2[mb], 0, 0, 0);
         }
+      }
+      if constexpr (NB == 1) {
+        // Add the other half of the logit from the partner wave (wave ^ 1), half 0 first.
+        floatx4* xch = reinterpret_cast<floatx4*>(smem + 2 * G::kTileBytes);
+        xch[(wave * 2 + 0) * 64 + lane] = s2[0];
+        xch[(wave * 2 + 1) * 64 + lane] = s2[1];
+        lds_barrier();
+        const floatx4 o0 = xch[((wave ^ 1) * 2 + 0) * 64 + lane];
+        const floatx4 o1 = xch[((wave ^ 1) * 2 + 1) * 64 + lane];
+        s2[0] = cp == 0 ? s2[0] + o0 : o0 + s2[0];
+        s2[1] = cp == 0 ? s2[1] + o1 : o1 + s2[1];
       }
       float sv[8];
 #pragma unroll
@@ -761,9 +795,8 @@ void decode_hs_kernel(DecodeArgs a) {
       }
       l_run += psum;
 
-      // O^T[channel][head] += V^T P^T. K index 8*g + e is token 16*(e>>2) + 4*g + (e&3), whose
-      // row has tau & 7 = 4*(g&1) + (e&3). M-block 4*blk + q holds channel
-      // 256*cp + 64*blk + 4*m + q in row m = n16.
+      // O^T[channel][head] += V^T P^T. K index 8*g + e is token 16*(e>>2) + 4*g + (e&3).
+      // M-block 4*blk + q holds channel 256*cp + 64*blk + 4*m + q in row m = n16.
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
         const int chunk = ((256 * cp + 64 * blk) >> 3) + (n16 >> 1);
@@ -771,7 +804,7 @@ void decode_hs_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int tau = 16 * (e >> 2) + 4 * g + (e & 3);
-          d[e] = *reinterpret_cast<const u32x2*>(buf + tau * G::kLatRow + ((chunk ^ (4 * (g & 1) + (e & 3))) << 4) +
+          d[e] = *reinterpret_cast<const u32x2*>(buf + tau * G::kLatRow + ((chunk ^ lat_swizzle(tau)) << 4) +
                                                  ((n16 & 1) << 3));
         }
 #pragma unroll
