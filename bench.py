@@ -61,14 +61,26 @@ def algorithmic_bytes(inp):
     return dict(decode_kernel=cache + q + meta, step=cache + q + meta + wuv + out, cache=cache)
 
 
+# The files the attention kernel is compiled from: a counter record taken on other sources is void.
+KERNEL_SOURCES = ("long_context_decode_mlra_amd/csrc/mlra_attention.hip",
+                  "long_context_decode_mlra_amd/csrc/mlra_device.h",
+                  "long_context_decode_mlra_amd/csrc/mlra_internal.h", "include/mlra.h")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_record(workload_name):
     """Counter-measured HBM bytes per decode-kernel launch, valid only for the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"traffic_decode_{workload_name}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "long_context_decode_mlra_amd", "csrc", "mlra_decode.hip"), "rb").read()
-    if rec.get("kernel_source_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
     return rec
 
@@ -95,14 +107,13 @@ def record_traffic(fetch_csv, write_csv, args):
     fetch = pick(f, "decode_kernel") * 1024 * f_scale
     write = pick(wr, "decode_kernel") * 1024 * w_scale
     ab = algorithmic_bytes(inp)
-    src = open(os.path.join(ROOT, "long_context_decode_mlra_amd", "csrc", "mlra_decode.hip"), "rb").read()
     rec = {"workload": w.name, "kernel": "decode_kernel", "fetch_bytes_per_launch": round(fetch),
            "write_bytes_per_launch": round(write), "hbm_bytes_per_launch": round(fetch + write),
            "algorithmic_bytes_per_launch": ab["decode_kernel"],
            "traffic_over_algorithmic": round((fetch + write) / ab["decode_kernel"], 4),
            "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
            "calibration": f"copy_kernel of {copy_bytes} bytes read and written in the same runs",
-           "kernel_source_sha256": hashlib.sha256(src).hexdigest()}
+           "kernel_sources": list(KERNEL_SOURCES), "kernel_source_sha256": kernel_source_hash()}
     out = os.path.join(ROOT, "profiles", f"traffic_decode_{w.name}.json")
     json.dump(rec, open(out, "w"), indent=1)
     print(json.dumps(rec))

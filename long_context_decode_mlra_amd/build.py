@@ -10,6 +10,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -17,6 +18,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmlra.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
+
+# HIP translation units of the library, compiled in parallel.
+HIP_SOURCES = ("mlra_attention.hip", "mlra_combine.hip", "mlra_absorb.hip", "mlra_probes.hip")
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are kept out of every kernel.
@@ -43,16 +47,20 @@ def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     params_o = os.path.join(BUILD_DIR, "mlra_params.o")
-    decode_o = os.path.join(BUILD_DIR, "mlra_decode.o")
     # Host-only C++ (no HIP): validation and workspace sizing.
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-c",
           os.path.join(CSRC, "mlra_params.cpp"), "-o", params_o])
-    out = _run([hipcc, *HIP_FLAGS, "-Wall", "-I", INCLUDE, "-c", os.path.join(CSRC, "mlra_decode.hip"),
-                "-o", decode_o])
-    if verbose and out.strip():
-        print(out)
+    objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in HIP_SOURCES]
+    with ThreadPoolExecutor(max_workers=len(HIP_SOURCES)) as ex:
+        outs = list(ex.map(lambda so: _run([hipcc, *HIP_FLAGS, "-Wall", "-I", INCLUDE, "-c",
+                                            os.path.join(CSRC, so[0]), "-o", so[1]]),
+                           zip(HIP_SOURCES, objs)))
+    if verbose:
+        for o in outs:
+            if o.strip():
+                print(o)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", params_o, decode_o, "-o", tmp])
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", params_o, *objs, "-o", tmp])
     os.replace(tmp, LIB)
     return LIB
 

@@ -9,37 +9,27 @@
 // ("Key Contributions" #2, #3). Each branch's logit adds the shared RoPE logit
 // (per-branch logit space 128 + 64, "Key Contributions" #2).
 //
-// Kernels
-//   decode_kernel   one workgroup per split; streams 32-token tiles of the cache
-//                   (latent rows + RoPE rows) HBM -> registers -> LDS, computes
-//                   S^T = K Q^T and O^T += V^T P^T on bf16 (or fp32) MFMA for all
-//                   query heads of the split's sequence, keeps an fp32 online
-//                   softmax per (latent head, query head), and writes one partial
-//                   (unnormalised O, running max, running sum) per sequence it touches.
-//   combine_kernel  log-sum-exp merge of each sequence's split partials and the W_UV
-//                   up-projection on fp32 MFMA, per 128-channel block of the latent.
-//   finalize_kernel the branch sum of the projected blocks and the output scale.
-// Splitting is balanced over the flattened tiles of all sequences (the plan).
+// Kernels (the split partials they write are merged by mlra_combine.hip)
+//   decode_kernel     one workgroup per split; streams 32-token tiles of the cache
+//                     (latent rows + RoPE rows) HBM -> LDS, computes S^T = K Q^T and
+//                     O^T += V^T P^T on bf16 (or fp32) MFMA for all query heads of the
+//                     split's sequence, keeps an fp32 online softmax per (latent head,
+//                     query head), and writes one partial (unnormalised O, running max,
+//                     running sum) per sequence it touches. MLRA-4 bf16, every fp32 form.
+//   decode_hs_kernel  the same for bf16 with one or two latent heads (MLA, MLRA-2), with
+//                     the query heads split across wave pairs.
+// Splitting is balanced over the flattened tiles of all sequences (the plan in mlra_device.h).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 #include <mutex>
 
-#include "mlra_internal.h"
+#include "mlra_device.h"
 
 namespace mlra {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float floatx2 __attribute__((ext_vector_type(2)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
 // Cache policy of the cache-tile loads: non-temporal. Every cache byte is read once per
 // step, so allocating it in L2 / the Infinity Cache only evicts useful lines; streaming
 // loads measured about 7 TB/s against about 6.1 TB/s for default-policy loads on MI355X.
@@ -49,11 +39,6 @@ constexpr int kStreamPolicy = 2;
 #define MLRA_DMA_STAGES 2
 #endif
 
-// Wave-uniform read of read-only metadata through the scalar data cache. Scalar loads
-// are counted by lgkmcnt, so they never wait on the tile loads in flight.
-__device__ __forceinline__ int32_t scalar_read(const int32_t* p) {
-  return *(const __attribute__((address_space(4))) int32_t*)p;
-}
 
 // Wait until at most n of this wave's vector-memory operations are outstanding
 // (n is a small compile-time-bounded count; s_waitcnt takes an immediate).
@@ -70,135 +55,6 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 // log2 units, so exp2 arguments stay <= 8 and unneeded rescales are skipped.
 // The final result is exact either way: numerator and denominator share the max.
 constexpr float kRescaleSlack = 8.0f;
-
-// ------------------------------------------------------------------ split plan
-// All sequences are cut into tiles of kTile tokens; the T tiles, taken in
-// sequence order, are cut into G = min(G_req, T) contiguous ranges of
-// floor/ceil(T/G) tiles. Range g = [g*T/G, (g+1)*T/G). Split g writes its
-// partial for sequence b into slot g + b: ranges are ordered, so the sequences
-// split g touches are >= those of any earlier split, which makes g + b unique.
-
-__device__ __forceinline__ int64_t tiles_of(int L) { return (int64_t(L) + kTile - 1) / kTile; }
-
-struct Plan {
-  int64_t T;
-  int G;
-};
-
-__device__ __forceinline__ int64_t wave_sum(int64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-// Every lane of the calling wave gets the same plan.
-__device__ Plan make_plan(const int32_t* __restrict__ seqlens, int B, int G_req) {
-  const int lane = threadIdx.x & 63;
-  int64_t s = 0;
-  for (int b = lane; b < B; b += 64) s += tiles_of(seqlens[b]);
-  Plan p;
-  p.T = wave_sum(s);
-  p.G = int(p.T < G_req ? p.T : G_req);
-  return p;
-}
-
-__device__ __forceinline__ int64_t split_begin(int64_t g, const Plan& p) { return g * p.T / p.G; }
-
-// Largest split g whose range starts at or before tile x (x < T): the split holding tile x.
-__device__ __forceinline__ int64_t split_of_tile(int64_t x, const Plan& p) {
-  return ((x + 1) * p.G - 1) / p.T;
-}
-
-// Inclusive prefix sum over the 64 lanes.
-__device__ __forceinline__ int64_t wave_inclusive_scan(int64_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int64_t y = __shfl_up(v, off, 64);
-    if (lane >= off) v += y;
-  }
-  return v;
-}
-
-// The sequence b holding global tile x (< T) and its first global tile P_b.
-__device__ void find_sequence(const int32_t* __restrict__ seqlens, int B, int64_t x, int& b_out,
-                              int64_t& P_out) {
-  const int lane = threadIdx.x & 63;
-  int64_t carry = 0;
-  for (int base = 0; base < B; base += 64) {
-    const int b = base + lane;
-    const int64_t t = b < B ? tiles_of(seqlens[b]) : 0;
-    const int64_t incl = wave_inclusive_scan(t);
-    const int64_t excl = carry + incl - t;
-    const unsigned long long hit = __ballot(b < B && t > 0 && excl <= x && x < excl + t);
-    if (hit) {
-      const int src = __ffsll(hit) - 1;
-      b_out = base + src;
-      P_out = __shfl(excl, src, 64);
-      return;
-    }
-    carry += __shfl(incl, 63, 64);
-  }
-  b_out = B;
-  P_out = carry;
-}
-
-// prefix[b] = first global tile of sequence b (b <= B), prefix[B+1] = T, prefix[B+2] = G.
-// Called by one whole wave.
-__device__ void write_prefix(const int32_t* __restrict__ seqlens, int B, const Plan& p, int64_t* prefix) {
-  const int lane = threadIdx.x & 63;
-  int64_t carry = 0;
-  for (int base = 0; base < B; base += 64) {
-    const int b = base + lane;
-    const int64_t t = b < B ? tiles_of(seqlens[b]) : 0;
-    const int64_t incl = wave_inclusive_scan(t);
-    if (b < B) prefix[b] = carry + incl - t;
-    carry += __shfl(incl, 63, 64);
-  }
-  if (lane == 0) {
-    prefix[B] = carry;
-    prefix[B + 1] = p.T;
-    prefix[B + 2] = p.G;
-  }
-}
-
-struct SegmentWalk {
-  int b;       // current sequence
-  int64_t Pb;  // its first global tile
-  int64_t cur; // next global tile to hand out
-  int64_t end; // end of this split's range
-};
-
-__device__ SegmentWalk begin_walk(const int32_t* __restrict__ seqlens, int B, int64_t g, const Plan& p) {
-  SegmentWalk w;
-  w.cur = split_begin(g, p);
-  w.end = split_begin(g + 1, p);
-  find_sequence(seqlens, B, w.cur, w.b, w.Pb);
-  return w;
-}
-
-// Next (sequence, first tile, end tile) of the split, tiles local to the sequence.
-__device__ bool next_segment(const int32_t* __restrict__ seqlens, int B, SegmentWalk& w, int& b, int& ta,
-                             int& te) {
-  while (w.cur < w.end && w.b < B) {
-    const int64_t n = tiles_of(seqlens[w.b]);
-    const int64_t seg_end = w.end < w.Pb + n ? w.end : w.Pb + n;
-    if (n > 0 && w.cur < seg_end) {
-      b = w.b;
-      ta = int(w.cur - w.Pb);
-      te = int(seg_end - w.Pb);
-      w.cur = seg_end;
-      if (seg_end == w.Pb + n) {
-        w.Pb += n;
-        ++w.b;
-      }
-      return true;
-    }
-    w.Pb += n;
-    ++w.b;
-  }
-  return false;
-}
 
 // ------------------------------------------------------------------ decode kernel
 
@@ -847,327 +703,9 @@ void decode_hs_kernel(DecodeArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ combine kernel
-//
-// One workgroup per (query head i, block q of kCombBlock of the 512 latent channels, group of
-// up to 32 sequences). Block q lies in latent head j = q*kCombBlock / d_latent, channels
-// c0..c0+kCombBlock-1 of it, c0 = q*kCombBlock % d_latent.
-//  1. merge:   obar[b][k] = sum_s 2^{m_s-M} O_s[c0+k] / sum_s 2^{m_s-M} l_s over the splits
-//              s holding part of sequence b (slots g + b, g in [g_first, g_last]), into LDS.
-//  2. project: y_q[b][d] = sum_k obar[b][k] * W_UV[j][i][c0+k][d] on fp32 MFMA
-//              (M = sequences, N = 128 output channels, K = kCombBlock). Every W_UV row is
-//              read by exactly one workgroup of the grid.
-//  y_q goes to the workspace; finalize_kernel adds the blocks in the fixed order q = 0, 1, ...
-//  (the branch sum) and applies out_scale. (Summing inside this kernel would need
-//  device-scope fences between workgroups on different L2 slices; their write-back and
-//  invalidate cost more than the extra launch.)
-
-struct CombineArgs {
-  const float* part_o;
-  const float* part_ml;
-  const int64_t* prefix;
-  const float* W_UV;
-  float* ypart;    // [groups][h][kCombBlocks][32][128]
-  int B, h;
-};
-
-constexpr int kCombSeqs = 32;
-constexpr int kCombBlocks = kLatentTotal / kCombBlock;
-constexpr int kCombTPS = kCombBlock / 16;  // merge threads per sequence, 4 channel quads each
-
-struct MergeState {
-  float M, den;
-  floatx4 acc[4];
-};
-
-// Fold one unnormalised partial (max m, sum l, four channel quads o) into st.
-__device__ __forceinline__ void merge_in(MergeState& st, float m, float l, const floatx4 (&o)[4]) {
-  if (m == -INFINITY) return;
-  if (m > st.M) {
-    const float sc = __builtin_amdgcn_exp2f(st.M - m);  // 0 when st.M is -inf
-    st.den *= sc;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) st.acc[u] *= sc;
-    st.M = m;
-  }
-  const float w = __builtin_amdgcn_exp2f(m - st.M);
-  st.den = fmaf(w, l, st.den);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) st.acc[u] += w * o[u];
-}
-
-template <int NB>
-__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  constexpr int DL = kLatentTotal / NB;
-  constexpr int kBatch = 4;  // slots loaded together
-  constexpr int kSteps = kCombBlock / 2;  // K steps of the 32x32x2 MFMA
-  __shared__ float ob[kCombBlock][kCombSeqs];  // merged block, k-major: ob[k][b]
-  __shared__ float st_red[18 * 256];            // per (slot part, pair): M, den, acc[16] (parts > 1)
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int i = blockIdx.x;
-  const int q = blockIdx.y;
-  const int grp = blockIdx.z;
-  const int j = (q * kCombBlock) / DL;
-  const int c0 = (q * kCombBlock) % DL;
-  const int b0 = grp * kCombSeqs;
-  const int nb = min(kCombSeqs, a.B - b0);
-  const int n = lane & 31, hh = lane >> 5;
-
-  // The W_UV slice this wave multiplies by (rows c0 + 2kb + hh, column 32*wave + n), issued
-  // first so that the loads overlap the merge.
-  const float* wcol = a.W_UV + ((int64_t(j) * a.h + i) * DL + c0) * kDV + 32 * wave + n;
-  float wv[kSteps];
-#pragma unroll
-  for (int kb = 0; kb < kSteps; ++kb) wv[kb] = wcol[(2 * kb + hh) * kDV];
-  __builtin_amdgcn_sched_barrier(0);
-
-  const Plan plan{a.prefix[a.B + 1], int(a.prefix[a.B + 2])};
-
-  // ---- 1. merge. kCombTPS threads per sequence, each owning channel quads cq0 + kCombTPS*v
-  // (v < 4); with nbp = nb rounded up to a power of two, S = 256 / (nbp * kCombTPS) slot
-  // parts share a sequence.
-  int nbp = 1;
-  while (nbp < nb) nbp <<= 1;
-  const int NPP = nbp * kCombTPS;  // threads per slot part
-  const int S = 256 / NPP;
-  const int r = tid / NPP;
-  const int rem = tid % NPP;
-  const int bl = rem / kCombTPS;
-  const int cq0 = rem % kCombTPS;
-  const bool live = bl < nb;
-  const int b = b0 + (live ? bl : 0);
-
-  MergeState st;
-  st.M = -INFINITY;
-  st.den = 0.f;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) st.acc[u] = floatx4{};
-  if (live) {
-    const int64_t P0 = a.prefix[b], P1 = a.prefix[b + 1];
-    if (P1 > P0) {
-      const int64_t gf = split_of_tile(P0, plan), gl = split_of_tile(P1 - 1, plan);
-      for (int64_t g = gf + r; g <= gl; g += kBatch * S) {
-        floatx2 ml[kBatch];
-        floatx4 o[kBatch][4];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int64_t gg = g + int64_t(u) * S;
-          const int64_t row = ((min(gg, gl) + b) * NB + j) * a.h + i;
-          ml[u] = *reinterpret_cast<const floatx2*>(a.part_ml + row * 2);
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            o[u][v] = *reinterpret_cast<const floatx4*>(a.part_o + row * DL + c0 + 4 * (cq0 + kCombTPS * v));
-          if (gg > gl) ml[u][0] = -INFINITY;  // past the end: re-read the last slot, then skip it
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) merge_in(st, ml[u][0], ml[u][1], o[u]);
-      }
-    }
-  }
-  if (S > 1) {
-    // Part r, field f (M, den, 16 accumulators), pair rem at st_red[(r * 18 + f) * NPP + rem].
-    if (live) {
-      st_red[(r * 18 + 0) * NPP + rem] = st.M;
-      st_red[(r * 18 + 1) * NPP + rem] = st.den;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st_red[(r * 18 + 2 + 4 * u + e) * NPP + rem] = st.acc[u][e];
-    }
-    __syncthreads();
-    if (live && r == 0) {
-      for (int rr = 1; rr < S; ++rr) {  // fixed order: part 0, 1, 2, ...
-        const float* sr = st_red + rr * 18 * NPP + rem;
-        floatx4 o1[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          o1[u] = floatx4{sr[(2 + 4 * u) * NPP], sr[(3 + 4 * u) * NPP], sr[(4 + 4 * u) * NPP], sr[(5 + 4 * u) * NPP]};
-        // Each part is an unnormalised partial of the same form as a split's.
-        merge_in(st, sr[0], sr[NPP], o1);
-      }
-    }
-  }
-  if (r == 0) {
-    const float inv = (live && st.den > 0.f) ? 1.f / st.den : 0.f;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int k = 4 * (cq0 + kCombTPS * v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ob[k + e][bl] = live ? st.acc[v][e] * inv : 0.f;
-    }
-  }
-  // Sequences of the padded group beyond nbp read as zero.
-  for (int idx = tid; idx < kCombBlock * kCombSeqs; idx += 256)
-    if ((idx % kCombSeqs) >= nbp) ob[idx / kCombSeqs][idx % kCombSeqs] = 0.f;
-  __syncthreads();
-
-  // ---- 2. project: wave w computes output channels [32w, 32w+32) for all 32 sequences.
-  floatx16 y = {};
-#pragma unroll
-  for (int kb = 0; kb < kSteps; ++kb) y = __builtin_amdgcn_mfma_f32_32x32x2f32(ob[2 * kb + hh][n], wv[kb], y, 0, 0, 0);
-
-  float* yq = a.ypart + ((int64_t(grp) * a.h + i) * kCombBlocks + q) * (kCombSeqs * kDV);
-#pragma unroll
-  for (int rr = 0; rr < 16; ++rr) yq[(8 * (rr >> 2) + 4 * hh + (rr & 3)) * kDV + 32 * wave + n] = y[rr];
-}
-
-// out[b][i][:] = out_scale * (y_0 + y_1 + ...)[b][:], blocks added in this order.
-struct FinalizeArgs {
-  const float* ypart;
-  float* out;
-  int B, h;
-  float out_scale;
-};
-
-__global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
-  const int64_t n4 = int64_t(a.B) * a.h * (kDV / 4);
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= n4) return;
-  const int d4 = int(idx % (kDV / 4));
-  const int64_t bi = idx / (kDV / 4);
-  const int i = int(bi % a.h);
-  const int b = int(bi / a.h);
-  const int grp = b / kCombSeqs, bl = b % kCombSeqs;
-  const floatx4* y = reinterpret_cast<const floatx4*>(
-                         a.ypart + ((int64_t(grp) * a.h + i) * kCombBlocks) * (kCombSeqs * kDV) + bl * kDV) + d4;
-  constexpr int kBlk = kCombSeqs * kDV / 4;
-  floatx4 v = y[0];
-#pragma unroll
-  for (int qq = 1; qq < kCombBlocks; ++qq) v += y[qq * kBlk];
-  reinterpret_cast<floatx4*>(a.out)[idx] = a.out_scale * v;
-}
-
-// ------------------------------------------------------------------ query-side absorption
-//
-// q_nope[b][i][j*DL + c] = sum_n W_UK[j][i][c][n] * q_pre[b][i][j][n] (decode step 1: the
-// NoPE key of head i in latent head j is C_j @ W_UK[j][i], so its dot with q_pre equals the
-// dot of C_j with W_UK[j][i] @ q_pre). One workgroup per (query head i, 128-row block r of the
-// 512 latent channels, group of 32 sequences); fp32 MFMA with M = sequences, N = latent
-// channels (32 per wave), K = d_nope = 128. The query block is staged in LDS k-major.
-
-struct AbsorbArgs {
-  const unsigned char* q_pre;
-  const float* W_UK;  // [NB][h][DL][128]
-  unsigned char* q_nope;
-  int B, h, NB;
-  int64_t qp_sb, qp_sh, qp_sj;  // bytes
-  int64_t qn_sb, qn_sh;         // bytes
-};
-
-constexpr int kDNope = 128;
-
-template <typename T>
-__global__ __launch_bounds__(256) void absorb_kernel(AbsorbArgs a) {
-  __shared__ float qs[kDNope][kCombSeqs];  // q_pre block, k-major: qs[n][b]
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 31, hh = lane >> 5;
-  const int i = blockIdx.x;
-  const int r = blockIdx.y;
-  const int grp = blockIdx.z;
-  const int DL = kLatentTotal / a.NB;
-  const int j = (r * 128) / DL;
-  const int c0 = (r * 128) % DL;
-  const int b0 = grp * kCombSeqs;
-  const int nb = min(kCombSeqs, a.B - b0);
-
-  // W_UK rows c0 + 32*wave + n, pairs of columns (k = 4*kp + 2*hh + e, e = 0, 1).
-  const float* wrow = a.W_UK + ((int64_t(j) * a.h + i) * DL + c0 + 32 * wave + n) * kDNope + 2 * hh;
-  floatx2 wv[kDNope / 4];
-#pragma unroll
-  for (int kp = 0; kp < kDNope / 4; ++kp) wv[kp] = *reinterpret_cast<const floatx2*>(wrow + 4 * kp);
-
-  for (int idx = tid; idx < kCombSeqs * kDNope; idx += 256) {
-    const int bl = idx / kDNope, k = idx % kDNope;
-    float v = 0.f;
-    if (bl < nb) {
-      const unsigned char* src = a.q_pre + int64_t(b0 + bl) * a.qp_sb + int64_t(i) * a.qp_sh + int64_t(j) * a.qp_sj;
-      v = float(reinterpret_cast<const T*>(src)[k]);
-    }
-    qs[k][bl] = v;
-  }
-  __syncthreads();
-
-  floatx16 y = {};
-#pragma unroll
-  for (int kp = 0; kp < kDNope / 4; ++kp) {
-    y = __builtin_amdgcn_mfma_f32_32x32x2f32(qs[4 * kp + 2 * hh][n], wv[kp][0], y, 0, 0, 0);
-    y = __builtin_amdgcn_mfma_f32_32x32x2f32(qs[4 * kp + 2 * hh + 1][n], wv[kp][1], y, 0, 0, 0);
-  }
-  // y[rr]: sequence 8*(rr>>2) + 4*hh + (rr&3), latent channel c0 + 32*wave + n.
-#pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    const int bl = 8 * (rr >> 2) + 4 * hh + (rr & 3);
-    if (bl < nb) {
-      T* dst = reinterpret_cast<T*>(a.q_nope + int64_t(b0 + bl) * a.qn_sb + int64_t(i) * a.qn_sh);
-      dst[j * DL + c0 + 32 * wave + n] = T(y[rr]);
-    }
-  }
-}
-
-// ------------------------------------------------------------------ plan dump and copy probe
-
-__global__ __launch_bounds__(64) void plan_kernel(const int32_t* seqlens, int B, int G_req, int max_seg,
-                                                  int32_t* out) {
-  const int g = blockIdx.x;
-  const int lane = threadIdx.x;
-  int32_t* row = out + int64_t(g) * max_seg * 3;
-  for (int k = lane; k < max_seg * 3; k += 64) row[k] = -1;
-  const Plan plan = make_plan(seqlens, B, G_req);
-  if (g == 0 && lane == 0) {
-    out[int64_t(G_req) * max_seg * 3] = int32_t(plan.T);
-    out[int64_t(G_req) * max_seg * 3 + 1] = plan.G;
-  }
-  if (g >= plan.G) return;
-  SegmentWalk walk = begin_walk(seqlens, B, g, plan);
-  int b, ta, te, k = 0;
-  while (next_segment(seqlens, B, walk, b, ta, te)) {
-    if (lane == 0 && k < max_seg) {
-      row[3 * k] = b;
-      row[3 * k + 1] = ta;
-      row[3 * k + 2] = te;
-    }
-    ++k;
-  }
-}
-
-// Read-only stream: each workgroup reads one contiguous chunk with non-temporal 16-byte
-// loads, 16 per thread in flight; the XOR of every word goes to sink[0] once per wave.
-constexpr int kReadUnroll = 16;
-
-__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n, int64_t per_wg,
-                                                   uint32_t* sink) {
-  const int64_t begin = int64_t(blockIdx.x) * per_wg;
-  const int64_t end = begin + per_wg < n ? begin + per_wg : n;
-  u32x4 x = {};
-  int64_t i = begin + threadIdx.x;
-  for (; i + (kReadUnroll - 1) * 256 < end; i += kReadUnroll * 256) {
-    u32x4 v[kReadUnroll];
-#pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) v[u] = __builtin_nontemporal_load(src + i + u * 256);
-#pragma unroll
-    for (int u = 0; u < kReadUnroll; ++u) x ^= v[u];
-  }
-  for (; i < end; i += 256) x ^= __builtin_nontemporal_load(src + i);
-  uint32_t r = x[0] ^ x[1] ^ x[2] ^ x[3];
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) r ^= __shfl_xor(r, off, 64);
-  if ((threadIdx.x & 63) == 0) atomicXor(sink, r);
-}
-
-__global__ __launch_bounds__(256) void copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                   int64_t n) {
-  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
-}
-
 // ------------------------------------------------------------------ host side
 
 using DecodeFn = void (*)(DecodeArgs);
-using CombineFn = void (*)(CombineArgs);
 
 DecodeFn pick_decode(int dtype, int nb, int hb) {
 #define MLRA_PICK(T, NB_)                                                        \
@@ -1183,18 +721,6 @@ DecodeFn pick_decode(int dtype, int nb, int hb) {
   }
 #undef MLRA_PICK
   return nullptr;
-}
-
-CombineFn pick_combine(int nb) {
-  switch (nb) {
-    case 4: return combine_kernel<4>;
-    case 2: return combine_kernel<2>;
-    default: return combine_kernel<1>;
-  }
-}
-
-int hip_fail(hipError_t e, const char* what) {
-  return set_error(MLRA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
 // Resident decode workgroups per device, cached per (device, kernel).
@@ -1227,25 +753,6 @@ int resident_splits(const mlra_decode_params& p, int32_t* out) {
     cache[dev][p.dtype][nbi][hb - 1] = n;
   }
   *out = n;
-  return MLRA_OK;
-}
-
-bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
-
-int prepare(const mlra_decode_params* p, const int32_t* seqlens, void* workspace, size_t workspace_bytes,
-            int32_t* G, WorkspaceLayout* lay) {
-  int rc = mlra_check_params(p);
-  if (rc) return rc;
-  rc = mlra_decode_num_splits(p, G);
-  if (rc) return rc;
-  *lay = workspace_layout(*p, *G);
-  if (p->batch == 0) return MLRA_OK;
-  if (!seqlens) return set_error(MLRA_ERR_NULL, "seqlens is NULL");
-  if (!workspace) return set_error(MLRA_ERR_WORKSPACE, "workspace is NULL");
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
-    return set_error(MLRA_ERR_ALIGN, "workspace must be 256-byte aligned");
-  if (workspace_bytes < lay->total)
-    return set_error(MLRA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, lay->total);
   return MLRA_OK;
 }
 
@@ -1324,130 +831,3 @@ extern "C" int mlra_decode_splitkv(const void* q_nope, const void* q_rope, const
   return MLRA_OK;
 }
 
-extern "C" int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, float* out,
-                                   const mlra_decode_params* p, void* workspace, size_t workspace_bytes,
-                                   void* stream) {
-  int32_t G = 0;
-  WorkspaceLayout lay;
-  int rc = prepare(p, seqlens, workspace, workspace_bytes, &G, &lay);
-  if (rc) return rc;
-  if (p->batch == 0) return MLRA_OK;
-  if (!W_UV || !out) return set_error(MLRA_ERR_NULL, "W_UV and out must be non-NULL");
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  CombineArgs c;
-  c.part_o = reinterpret_cast<const float*>(ws + lay.part_o_off);
-  c.part_ml = reinterpret_cast<const float*>(ws + lay.part_ml_off);
-  c.prefix = reinterpret_cast<const int64_t*>(ws + lay.prefix_off);
-  c.W_UV = W_UV;
-  c.ypart = reinterpret_cast<float*>(ws + lay.ypart_off);
-  c.B = p->batch;
-  c.h = p->num_heads;
-  const dim3 grid(p->num_heads, kCombBlocks, (p->batch + kCombSeqs - 1) / kCombSeqs);
-  hipLaunchKernelGGL(pick_combine(p->num_branches), grid, dim3(256), 0, static_cast<hipStream_t>(stream), c);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
-  FinalizeArgs f;
-  f.ypart = c.ypart;
-  f.out = out;
-  f.B = p->batch;
-  f.h = p->num_heads;
-  f.out_scale = p->out_scale;
-  const int64_t n4 = int64_t(p->batch) * p->num_heads * (kDV / 4);
-  hipLaunchKernelGGL(finalize_kernel, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), f);
-  e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "finalize kernel launch");
-  return MLRA_OK;
-}
-
-extern "C" int mlra_decode(const void* q_nope, const void* q_rope, const void* latent_cache, const void* rope_cache,
-                           const int32_t* block_table, const int32_t* seqlens, const float* W_UV, float* out,
-                           const mlra_decode_params* p, void* workspace, size_t workspace_bytes, void* stream) {
-  if (p && p->batch > 0 && (!W_UV || !out)) return set_error(MLRA_ERR_NULL, "W_UV and out must be non-NULL");
-  int rc = mlra_decode_splitkv(q_nope, q_rope, latent_cache, rope_cache, block_table, seqlens, p, workspace,
-                               workspace_bytes, stream);
-  if (rc) return rc;
-  return mlra_decode_combine(seqlens, W_UV, out, p, workspace, workspace_bytes, stream);
-}
-
-extern "C" int mlra_absorb_query(const void* q_pre, const float* W_UK, void* q_nope, const mlra_decode_params* p,
-                                 int32_t d_nope, int64_t qpre_stride_b, int64_t qpre_stride_h,
-                                 int64_t qpre_stride_j, void* stream) {
-  int rc = mlra_check_params(p);
-  if (rc) return rc;
-  if (d_nope != kDNope) return set_error(MLRA_ERR_UNSUPPORTED, "d_nope must be %d (got %d)", kDNope, d_nope);
-  if (qpre_stride_b < 0 || qpre_stride_h < 0 || qpre_stride_j < 0)
-    return set_error(MLRA_ERR_SHAPE, "query strides must be >= 0");
-  if (p->batch == 0) return MLRA_OK;
-  if (!q_pre || !W_UK || !q_nope) return set_error(MLRA_ERR_NULL, "q_pre, W_UK and q_nope must be non-NULL");
-  const int64_t esz = p->dtype == MLRA_BF16 ? 2 : 4;
-  AbsorbArgs a;
-  a.q_pre = static_cast<const unsigned char*>(q_pre);
-  a.W_UK = W_UK;
-  a.q_nope = static_cast<unsigned char*>(q_nope);
-  a.B = p->batch;
-  a.h = p->num_heads;
-  a.NB = p->num_branches;
-  a.qp_sb = qpre_stride_b * esz;
-  a.qp_sh = qpre_stride_h * esz;
-  a.qp_sj = qpre_stride_j * esz;
-  a.qn_sb = p->q_stride_b * esz;
-  a.qn_sh = p->q_stride_h * esz;
-  const dim3 grid(p->num_heads, kLatentTotal / 128, (p->batch + kCombSeqs - 1) / kCombSeqs);
-  if (p->dtype == MLRA_BF16)
-    hipLaunchKernelGGL(absorb_kernel<__bf16>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
-  else
-    hipLaunchKernelGGL(absorb_kernel<float>, grid, dim3(256), 0, static_cast<hipStream_t>(stream), a);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "absorb kernel launch");
-  return MLRA_OK;
-}
-
-extern "C" int mlra_decode_plan(const int32_t* seqlens, int32_t batch, int32_t num_splits, int32_t max_segments,
-                                int32_t* plan, void* stream) {
-  if (batch < 0 || num_splits < 1 || max_segments < 1)
-    return set_error(MLRA_ERR_SHAPE, "batch >= 0, num_splits >= 1 and max_segments >= 1 required");
-  if (!plan || (batch > 0 && !seqlens)) return set_error(MLRA_ERR_NULL, "seqlens and plan must be non-NULL");
-  hipLaunchKernelGGL(plan_kernel, dim3(num_splits), dim3(64), 0, static_cast<hipStream_t>(stream), seqlens, batch,
-                     num_splits, max_segments, plan);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "plan kernel launch");
-  return MLRA_OK;
-}
-
-extern "C" int mlra_read_bandwidth_probe(const void* src, size_t bytes, uint32_t* sink, void* stream) {
-  if (!src || !sink) return set_error(MLRA_ERR_NULL, "src and sink must be non-NULL");
-  if (!aligned16(src) || bytes % 16 != 0) return set_error(MLRA_ERR_ALIGN, "src and bytes must be 16-byte aligned");
-  if (bytes == 0) return MLRA_OK;
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return hip_fail(e, "device query");
-  const int64_t n = int64_t(bytes / 16);
-  const int64_t blocks = int64_t(cus) * 4;
-  const int64_t per_wg = (n + blocks - 1) / blocks;
-  hipLaunchKernelGGL(read_kernel, dim3(unsigned(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const u32x4*>(src), n, per_wg, sink);
-  e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "read kernel launch");
-  return MLRA_OK;
-}
-
-extern "C" int mlra_copy_bandwidth_probe(const void* src, void* dst, size_t bytes, void* stream) {
-  if (!src || !dst) return set_error(MLRA_ERR_NULL, "src and dst must be non-NULL");
-  if (!aligned16(src) || !aligned16(dst) || bytes % 16 != 0)
-    return set_error(MLRA_ERR_ALIGN, "src, dst and bytes must be 16-byte aligned");
-  if (bytes == 0) return MLRA_OK;
-  int dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e != hipSuccess) return hip_fail(e, "device query");
-  const int64_t n = int64_t(bytes / 16);
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > int64_t(cus) * 16) blocks = int64_t(cus) * 16;
-  hipLaunchKernelGGL(copy_kernel, dim3(unsigned(blocks)), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
-  e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "copy kernel launch");
-  return MLRA_OK;
-}

@@ -1,0 +1,268 @@
+// Split-KV combine for the decode of mlra_attention.hip: log-sum-exp merge of each
+// sequence's split partials, the W_UV up-projection on fp32 MFMA per block of latent
+// channels, and the branch sum with the output scale (page "Multi-Head Low-Rank
+// Attention", ai.info summary of arXiv 2603.02188, "Key Contributions" #2, #3).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "mlra_device.h"
+
+namespace mlra {
+namespace {
+
+// ------------------------------------------------------------------ combine kernel
+//
+// One workgroup per (query head i, block q of kCombBlock of the 512 latent channels, group of
+// up to 32 sequences). Block q lies in latent head j = q*kCombBlock / d_latent, channels
+// c0..c0+kCombBlock-1 of it, c0 = q*kCombBlock % d_latent.
+//  1. merge:   obar[b][k] = sum_s 2^{m_s-M} O_s[c0+k] / sum_s 2^{m_s-M} l_s over the splits
+//              s holding part of sequence b (slots g + b, g in [g_first, g_last]), into LDS.
+//  2. project: y_q[b][d] = sum_k obar[b][k] * W_UV[j][i][c0+k][d] on fp32 MFMA
+//              (M = sequences, N = 128 output channels, K = kCombBlock). Every W_UV row is
+//              read by exactly one workgroup of the grid.
+//  y_q goes to the workspace; finalize_kernel adds the blocks in the fixed order q = 0, 1, ...
+//  (the branch sum) and applies out_scale. (Summing inside this kernel would need
+//  device-scope fences between workgroups on different L2 slices; their write-back and
+//  invalidate cost more than the extra launch.)
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_ml;
+  const int64_t* prefix;
+  const float* W_UV;
+  float* ypart;    // [groups][h][kCombBlocks][32][128]
+  int B, h;
+};
+
+constexpr int kCombSeqs = 32;
+constexpr int kCombBlocks = kLatentTotal / kCombBlock;
+constexpr int kCombTPS = kCombBlock / 16;  // merge threads per sequence, 4 channel quads each
+
+struct MergeState {
+  float M, den;
+  floatx4 acc[4];
+};
+
+// Fold one unnormalised partial (max m, sum l, four channel quads o) into st.
+__device__ __forceinline__ void merge_in(MergeState& st, float m, float l, const floatx4 (&o)[4]) {
+  if (m == -INFINITY) return;
+  if (m > st.M) {
+    const float sc = __builtin_amdgcn_exp2f(st.M - m);  // 0 when st.M is -inf
+    st.den *= sc;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) st.acc[u] *= sc;
+    st.M = m;
+  }
+  const float w = __builtin_amdgcn_exp2f(m - st.M);
+  st.den = fmaf(w, l, st.den);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) st.acc[u] += w * o[u];
+}
+
+template <int NB>
+__global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
+  constexpr int DL = kLatentTotal / NB;
+  constexpr int kBatch = 4;  // slots loaded together
+  constexpr int kSteps = kCombBlock / 2;  // K steps of the 32x32x2 MFMA
+  __shared__ float ob[kCombBlock][kCombSeqs];  // merged block, k-major: ob[k][b]
+  __shared__ float st_red[18 * 256];            // per (slot part, pair): M, den, acc[16] (parts > 1)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int i = blockIdx.x;
+  const int q = blockIdx.y;
+  const int grp = blockIdx.z;
+  const int j = (q * kCombBlock) / DL;
+  const int c0 = (q * kCombBlock) % DL;
+  const int b0 = grp * kCombSeqs;
+  const int nb = min(kCombSeqs, a.B - b0);
+  const int n = lane & 31, hh = lane >> 5;
+
+  // The W_UV slice this wave multiplies by (rows c0 + 2kb + hh, column 32*wave + n), issued
+  // first so that the loads overlap the merge.
+  const float* wcol = a.W_UV + ((int64_t(j) * a.h + i) * DL + c0) * kDV + 32 * wave + n;
+  float wv[kSteps];
+#pragma unroll
+  for (int kb = 0; kb < kSteps; ++kb) wv[kb] = wcol[(2 * kb + hh) * kDV];
+  __builtin_amdgcn_sched_barrier(0);
+
+  const Plan plan{a.prefix[a.B + 1], int(a.prefix[a.B + 2])};
+
+  // ---- 1. merge. kCombTPS threads per sequence, each owning channel quads cq0 + kCombTPS*v
+  // (v < 4); with nbp = nb rounded up to a power of two, S = 256 / (nbp * kCombTPS) slot
+  // parts share a sequence.
+  int nbp = 1;
+  while (nbp < nb) nbp <<= 1;
+  const int NPP = nbp * kCombTPS;  // threads per slot part
+  const int S = 256 / NPP;
+  const int r = tid / NPP;
+  const int rem = tid % NPP;
+  const int bl = rem / kCombTPS;
+  const int cq0 = rem % kCombTPS;
+  const bool live = bl < nb;
+  const int b = b0 + (live ? bl : 0);
+
+  MergeState st;
+  st.M = -INFINITY;
+  st.den = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) st.acc[u] = floatx4{};
+  if (live) {
+    const int64_t P0 = a.prefix[b], P1 = a.prefix[b + 1];
+    if (P1 > P0) {
+      const int64_t gf = split_of_tile(P0, plan), gl = split_of_tile(P1 - 1, plan);
+      for (int64_t g = gf + r; g <= gl; g += kBatch * S) {
+        floatx2 ml[kBatch];
+        floatx4 o[kBatch][4];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int64_t gg = g + int64_t(u) * S;
+          const int64_t row = ((min(gg, gl) + b) * NB + j) * a.h + i;
+          ml[u] = *reinterpret_cast<const floatx2*>(a.part_ml + row * 2);
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            o[u][v] = *reinterpret_cast<const floatx4*>(a.part_o + row * DL + c0 + 4 * (cq0 + kCombTPS * v));
+          if (gg > gl) ml[u][0] = -INFINITY;  // past the end: re-read the last slot, then skip it
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) merge_in(st, ml[u][0], ml[u][1], o[u]);
+      }
+    }
+  }
+  if (S > 1) {
+    // Part r, field f (M, den, 16 accumulators), pair rem at st_red[(r * 18 + f) * NPP + rem].
+    if (live) {
+      st_red[(r * 18 + 0) * NPP + rem] = st.M;
+      st_red[(r * 18 + 1) * NPP + rem] = st.den;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st_red[(r * 18 + 2 + 4 * u + e) * NPP + rem] = st.acc[u][e];
+    }
+    __syncthreads();
+    if (live && r == 0) {
+      for (int rr = 1; rr < S; ++rr) {  // fixed order: part 0, 1, 2, ...
+        const float* sr = st_red + rr * 18 * NPP + rem;
+        floatx4 o1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          o1[u] = floatx4{sr[(2 + 4 * u) * NPP], sr[(3 + 4 * u) * NPP], sr[(4 + 4 * u) * NPP], sr[(5 + 4 * u) * NPP]};
+        // Each part is an unnormalised partial of the same form as a split's.
+        merge_in(st, sr[0], sr[NPP], o1);
+      }
+    }
+  }
+  if (r == 0) {
+    const float inv = (live && st.den > 0.f) ? 1.f / st.den : 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int k = 4 * (cq0 + kCombTPS * v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ob[k + e][bl] = live ? st.acc[v][e] * inv : 0.f;
+    }
+  }
+  // Sequences of the padded group beyond nbp read as zero.
+  for (int idx = tid; idx < kCombBlock * kCombSeqs; idx += 256)
+    if ((idx % kCombSeqs) >= nbp) ob[idx / kCombSeqs][idx % kCombSeqs] = 0.f;
+  __syncthreads();
+
+  // ---- 2. project: wave w computes output channels [32w, 32w+32) for all 32 sequences.
+  floatx16 y = {};
+#pragma unroll
+  for (int kb = 0; kb < kSteps; ++kb) y = __builtin_amdgcn_mfma_f32_32x32x2f32(ob[2 * kb + hh][n], wv[kb], y, 0, 0, 0);
+
+  float* yq = a.ypart + ((int64_t(grp) * a.h + i) * kCombBlocks + q) * (kCombSeqs * kDV);
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) yq[(8 * (rr >> 2) + 4 * hh + (rr & 3)) * kDV + 32 * wave + n] = y[rr];
+}
+
+// out[b][i][:] = out_scale * (y_0 + y_1 + ...)[b][:], blocks added in this order.
+struct FinalizeArgs {
+  const float* ypart;
+  float* out;
+  int B, h;
+  float out_scale;
+};
+
+__global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
+  const int64_t n4 = int64_t(a.B) * a.h * (kDV / 4);
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= n4) return;
+  const int d4 = int(idx % (kDV / 4));
+  const int64_t bi = idx / (kDV / 4);
+  const int i = int(bi % a.h);
+  const int b = int(bi / a.h);
+  const int grp = b / kCombSeqs, bl = b % kCombSeqs;
+  const floatx4* y = reinterpret_cast<const floatx4*>(
+                         a.ypart + ((int64_t(grp) * a.h + i) * kCombBlocks) * (kCombSeqs * kDV) + bl * kDV) + d4;
+  constexpr int kBlk = kCombSeqs * kDV / 4;
+  floatx4 v = y[0];
+#pragma unroll
+  for (int qq = 1; qq < kCombBlocks; ++qq) v += y[qq * kBlk];
+  reinterpret_cast<floatx4*>(a.out)[idx] = a.out_scale * v;
+}
+
+using CombineFn = void (*)(CombineArgs);
+
+CombineFn pick_combine(int nb) {
+  switch (nb) {
+    case 4: return combine_kernel<4>;
+    case 2: return combine_kernel<2>;
+    default: return combine_kernel<1>;
+  }
+}
+
+}  // namespace
+}  // namespace mlra
+
+using namespace mlra;
+
+extern "C" int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, float* out,
+                                   const mlra_decode_params* p, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  int32_t G = 0;
+  WorkspaceLayout lay;
+  int rc = prepare(p, seqlens, workspace, workspace_bytes, &G, &lay);
+  if (rc) return rc;
+  if (p->batch == 0) return MLRA_OK;
+  if (!W_UV || !out) return set_error(MLRA_ERR_NULL, "W_UV and out must be non-NULL");
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  CombineArgs c;
+  c.part_o = reinterpret_cast<const float*>(ws + lay.part_o_off);
+  c.part_ml = reinterpret_cast<const float*>(ws + lay.part_ml_off);
+  c.prefix = reinterpret_cast<const int64_t*>(ws + lay.prefix_off);
+  c.W_UV = W_UV;
+  c.ypart = reinterpret_cast<float*>(ws + lay.ypart_off);
+  c.B = p->batch;
+  c.h = p->num_heads;
+  const dim3 grid(p->num_heads, kCombBlocks, (p->batch + kCombSeqs - 1) / kCombSeqs);
+  hipLaunchKernelGGL(pick_combine(p->num_branches), grid, dim3(256), 0, static_cast<hipStream_t>(stream), c);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
+  FinalizeArgs f;
+  f.ypart = c.ypart;
+  f.out = out;
+  f.B = p->batch;
+  f.h = p->num_heads;
+  f.out_scale = p->out_scale;
+  const int64_t n4 = int64_t(p->batch) * p->num_heads * (kDV / 4);
+  hipLaunchKernelGGL(finalize_kernel, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), f);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "finalize kernel launch");
+  return MLRA_OK;
+}
+
+extern "C" int mlra_decode(const void* q_nope, const void* q_rope, const void* latent_cache, const void* rope_cache,
+                           const int32_t* block_table, const int32_t* seqlens, const float* W_UV, float* out,
+                           const mlra_decode_params* p, void* workspace, size_t workspace_bytes, void* stream) {
+  if (p && p->batch > 0 && (!W_UV || !out)) return set_error(MLRA_ERR_NULL, "W_UV and out must be non-NULL");
+  int rc = mlra_decode_splitkv(q_nope, q_rope, latent_cache, rope_cache, block_table, seqlens, p, workspace,
+                               workspace_bytes, stream);
+  if (rc) return rc;
+  return mlra_decode_combine(seqlens, W_UV, out, p, workspace, workspace_bytes, stream);
+}
+

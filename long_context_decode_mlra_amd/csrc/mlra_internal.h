@@ -1,4 +1,4 @@
-// Shared between the host-only parameter code and the HIP translation unit.
+// Shared between the host-only parameter code and the HIP translation units.
 // Holds no HIP types so that mlra_params.cpp builds as plain C++.
 #pragma once
 
@@ -42,5 +42,12 @@ int set_error(int code, const char* fmt, ...);
 void clear_error();
 
 int head_blocks(int num_heads);
+
+bool aligned16(const void* ptr);
+
+// Validates p, resolves the split count G and the workspace layout, and checks the
+// workspace pointer and size (B = 0 needs neither seqlens nor a workspace).
+int prepare(const mlra_decode_params* p, const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+            int32_t* G, WorkspaceLayout* lay);
 
 }  // namespace mlra

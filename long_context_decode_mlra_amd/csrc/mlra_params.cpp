@@ -42,6 +42,26 @@ WorkspaceLayout workspace_layout(const mlra_decode_params& p, int32_t num_splits
   return w;
 }
 
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+int prepare(const mlra_decode_params* p, const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+            int32_t* G, WorkspaceLayout* lay) {
+  int rc = mlra_check_params(p);
+  if (rc) return rc;
+  rc = mlra_decode_num_splits(p, G);
+  if (rc) return rc;
+  *lay = workspace_layout(*p, *G);
+  if (p->batch == 0) return MLRA_OK;
+  if (!seqlens) return set_error(MLRA_ERR_NULL, "seqlens is NULL");
+  if (!workspace) return set_error(MLRA_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return set_error(MLRA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < lay->total)
+    return set_error(MLRA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, lay->total);
+  return MLRA_OK;
+}
+
 }  // namespace mlra
 
 using namespace mlra;
