@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--num-splits", type=int, default=0, help="0 = one split per resident workgroup slot")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="also time steps each preceded by a write of this many MiB (cold L2 / Infinity Cache); 0 = skip")
     ap.add_argument("--copy-probe-mib", type=int, default=1024, help="size of the copy-kernel reference run")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of this "
@@ -104,10 +106,11 @@ def record_traffic(fetch_csv, write_csv, args):
     w_scale = copy_bytes / (pick(wr, "copy_kernel") * 1024)
     w = CONFIGS[args.config]
     inp = make_inputs(w, seed=args.config)
-    fetch = pick(f, "decode_kernel") * 1024 * f_scale
-    write = pick(wr, "decode_kernel") * 1024 * w_scale
+    attn = lambda d: next(v for k, v in d.items() if "decode_kernel" in k or "decode_hs_kernel" in k)
+    fetch = attn(f) * 1024 * f_scale
+    write = attn(wr) * 1024 * w_scale
     ab = algorithmic_bytes(inp)
-    rec = {"workload": w.name, "kernel": "decode_kernel", "fetch_bytes_per_launch": round(fetch),
+    rec = {"workload": w.name, "kernel": "split-KV attention kernel", "fetch_bytes_per_launch": round(fetch),
            "write_bytes_per_launch": round(write), "hbm_bytes_per_launch": round(fetch + write),
            "algorithmic_bytes_per_launch": ab["decode_kernel"],
            "traffic_over_algorithmic": round((fetch + write) / ab["decode_kernel"], 4),
@@ -213,10 +216,24 @@ def main():
     eager_ms = (t1 - t0) * 1e3 / args.steps
     ms_per_step = eager_ms
 
-    # Per-kernel durations in a separate loop: HIP events on the launch stream around the
-    # attention kernel and around the combine. (An event between launches idles the GPU for a
-    # few microseconds, so these steps are not the ones timed above.)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # Per-kernel durations, from HIP events on the launch stream. (1) The attention kernel
+    # launched K times back to back and the combine (combine + finalize) K times back to back,
+    # each run bracketed by one event pair: the mean launch duration. (2) Every step bracketed
+    # by its own events, for the spread; an event between launches idles the GPU for a few
+    # microseconds, so these per-launch figures run slightly high.
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ea, eb, ec = ev(), ev(), ev()
+    ea.record(stream)
+    for _ in range(args.steps):
+        dec.splitkv(stream)
+    eb.record(stream)
+    for _ in range(args.steps):
+        dec.combine(stream)
+    ec.record(stream)
+    torch.cuda.synchronize()
+    dk_mean = ea.elapsed_time(eb) / args.steps
+    ck_mean = eb.elapsed_time(ec) / args.steps
+    evs = [[ev() for _ in range(3)] for _ in range(args.steps)]
     for k in range(args.steps):
         evs[k][0].record(stream)
         dec.splitkv(stream)
@@ -224,6 +241,20 @@ def main():
         dec.combine(stream)
         evs[k][2].record(stream)
     torch.cuda.synchronize()
+    # (3) Cold caches: before each step an untimed write of flush_mib MiB evicts L2 and the
+    # Infinity Cache, then events bracket the whole step.
+    cold = None
+    if args.flush_mib > 0:
+        junk = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev)
+        cev = [(ev(), ev()) for _ in range(args.steps)]
+        for k in range(args.steps):
+            junk.fill_(float(k))
+            cev[k][0].record(stream)
+            dec(stream)
+            cev[k][1].record(stream)
+        torch.cuda.synchronize()
+        cold = sorted(a.elapsed_time(b) for a, b in cev)
+        del junk
     graph_ms = None
     if args.graph:
         # The same step recorded once as a HIP graph and replayed: the way a serving loop runs it.
@@ -255,9 +286,6 @@ def main():
         absorb = {"us_per_call": round(a_us, 2), "algorithmic_bytes": a_bytes,
                   "achieved_GBps": round(a_bytes / (a_us * 1e-6) / 1e9, 1)}
     dk = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    ck = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    dk_mean = sum(dk) / len(dk)
-    ck_mean = sum(ck) / len(ck)
 
     ab = algorithmic_bytes(inp)
     tokens = inp.total_tokens
@@ -268,7 +296,8 @@ def main():
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": (trec["hbm_bytes_per_launch"] if trec else None),
-                "kernel": "decode_kernel (split-KV attention)",
+                "kernel": ("decode_hs_kernel" if (w.dtype == "bf16" and w.NB < 4) else "decode_kernel")
+                          + " (split-KV attention)",
                 "algorithmic_bytes_per_launch": ab["decode_kernel"],
                 "avg_launch_us": round(dk_mean * 1e3, 2)}
     result = {
@@ -284,9 +313,14 @@ def main():
         "achieved_hbm_TBps": round(ab["step"] / (us * 1e-6) / 1e12, 3),
         "tokens_per_s": round(len(inp.seqlens) / (us * 1e-6), 1),
         "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4),
-        "kernels_us": {"decode_kernel_mean": round(dk_mean * 1e3, 2), "decode_kernel_p10": round(dk[len(dk) // 10] * 1e3, 2),
-                       "decode_kernel_p90": round(dk[(9 * len(dk)) // 10] * 1e3, 2),
-                       "combine_kernel_mean": round(ck_mean * 1e3, 2)},
+        "kernels_us": {"attention_kernel_mean": round(dk_mean * 1e3, 2),
+                       "attention_kernel_p10_event_bracketed": round(dk[len(dk) // 10] * 1e3, 2),
+                       "attention_kernel_p90_event_bracketed": round(dk[(9 * len(dk)) // 10] * 1e3, 2),
+                       "combine_and_finalize_mean": round(ck_mean * 1e3, 2)},
+        "cold_cache_us_per_step": None if cold is None else {
+            "median": round(cold[len(cold) // 2] * 1e3, 2), "p10": round(cold[len(cold) // 10] * 1e3, 2),
+            "p90": round(cold[(9 * len(cold)) // 10] * 1e3, 2),
+            "note": f"each step after an untimed {args.flush_mib} MiB write, events around the step"},
         "algorithmic_bytes_per_step": ab["step"],
         "copy_probe_GBps": None if copy_gbps is None else round(copy_gbps, 1),
         "read_probe_GBps": None if read_gbps is None else round(read_gbps, 1),

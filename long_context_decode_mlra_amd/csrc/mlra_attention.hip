@@ -40,17 +40,32 @@ constexpr int kStreamPolicy = 2;
 #endif
 
 
-// Wait until at most n of this wave's vector-memory operations are outstanding
-// (n is a small compile-time-bounded count; s_waitcnt takes an immediate).
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
-    case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
-    case 27: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+// Wait until at most N of this wave's vector-memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Wait until this wave's loads of the oldest tile in flight have landed, with `later`
+// (0 <= later < S, wave-uniform) tiles issued after it still allowed in flight. Wave w
+// issues Q + 1 loads per tile if w < R, else Q.
+template <int S, int Q, int R>
+__device__ __forceinline__ void wait_tile(int later, int wave) {
+  if constexpr (S > 1) {
+    if (later == S - 1) {
+      if (R > 0 && wave < R)
+        wait_vmcnt<(S - 1) * (Q + 1)>();
+      else
+        wait_vmcnt<(S - 1) * Q>();
+      return;
+    }
+    wait_tile<S - 1, Q, R>(later, wave);
+  } else {
+    wait_vmcnt<0>();
   }
 }
+
 // A running max is only raised once the tile max exceeds it by this many
 // log2 units, so exp2 arguments stay <= 8 and unneeded rescales are skipped.
 // The final result is exact either way: numerator and denominator share the max.
@@ -108,14 +123,16 @@ struct Geo {
   // Loads go straight into LDS unless the idle tile buffer is needed for the
   // logit exchange between the waves that share one latent head.
   static constexpr bool kDirect = (kWPB == 1);
-  // Tile buffers: with direct loads, one bf16 head block (every wave issues the same
-  // number of loads per tile) runs a deeper ring: kStages - 1 tiles in flight.
+  // Tile buffers: with direct loads, one bf16 head block may run a deeper ring (kStages
+  // tiles in flight while a wave waits for the oldest).
   static constexpr int kStages = (kDirect && kEsz == 2 && HB == 1) ? MLRA_DMA_STAGES : 2;
   static constexpr int kLds = kStages * kTileBytes;
   static_assert(kLatTile % 1024 == 0 && kTileBytes % 1024 == 0, "tile must be whole 1 KiB loads");
   static_assert(kWaves * 4096 <= kTileBytes, "logit exchange must fit the idle tile buffer");
-  static_assert(kStages == 2 || (kInstPerWave * kWaves == kInst && kInstPerWave == 9 && kStages <= 4),
-                "deep rings need equal per-wave load counts that wait_vmcnt knows");
+  // Wave w issues the tile load instructions w, w + kWaves, ... below kInst: kLoadsQ + 1
+  // of them if w < kLoadsR, else kLoadsQ.
+  static constexpr int kLoadsQ = kInst / kWaves;
+  static constexpr int kLoadsR = kInst % kWaves;
 };
 
 // Per-lane MFMA operands of the query: lane (n, hh) supplies query head 32*hb + n.
@@ -386,9 +403,10 @@ void decode_kernel(DecodeArgs a) {
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    // kStages LDS tile buffers. Direct loads: tiles k+1 .. k+kStages-1 are on their way
-    // into the other buffers while tile k is computed. Register staging: tile k+1 is in
-    // registers while tile k is computed.
+    // kStages LDS tile buffers. Direct loads: tile k+kStages-1 is issued before the wave
+    // waits for tile k, so kStages tiles are on their way while it waits and kStages-1
+    // while tile k is computed. Register staging: tile k+1 is in registers while tile k
+    // is computed.
     [[maybe_unused]] u32x4 stg[G::kDirect ? 1 : G::kInstPerWave];
     if constexpr (G::kDirect) {
 #pragma unroll
@@ -402,13 +420,15 @@ void decode_kernel(DecodeArgs a) {
       unsigned char* buf = smem + slot * G::kTileBytes;
       unsigned char* idle = smem + ((k - ta + 1) % G::kStages) * G::kTileBytes;
       if constexpr (G::kDirect) {
-        // This wave's loads of tile k have landed once at most the later tiles' loads are pending.
-        const int later = min(G::kStages - 2, te - 1 - k);
-        wait_vmcnt(G::kStages == 2 ? 0 : later * G::kInstPerWave);
-        lds_barrier();  // every wave's part landed; every wave is done with tile k-1's buffer
-        if (k + G::kStages - 1 < te)
+        if (k + G::kStages - 1 < te) {
+          // Tile k+kStages-1 reuses the buffer of tile k-1: every wave must be done with it.
+          if (k > ta) lds_barrier();
           issue_tile_dma<T, NB, HB>(a, b, L, k + G::kStages - 1, wave, lane,
                                     smem + ((k - ta + G::kStages - 1) % G::kStages) * G::kTileBytes);
+        }
+        // This wave's loads of tile k have landed once only the later tiles' loads are pending.
+        wait_tile<G::kStages, G::kLoadsQ, G::kLoadsR>(min(G::kStages - 1, te - 1 - k), wave);
+        lds_barrier();  // every wave's part of tile k landed
       } else {
         store_tile<T, NB, HB>(buf, wave, lane, stg);
         if (k + 1 < te) issue_tile_loads<T, NB, HB>(a, b, L, k + 1, wave, lane, stg);
@@ -570,9 +590,14 @@ void decode_hs_kernel(DecodeArgs a) {
     for (int k = ta; k < te; ++k) {
       unsigned char* buf = smem + ((k - ta) & 1) * G::kTileBytes;
       unsigned char* idle = smem + (((k - ta) & 1) ^ 1) * G::kTileBytes;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile k has landed
-      lds_barrier();  // every wave's part landed; every wave is done with tile k-1's buffer
-      if (k + 1 < te) issue_tile_dma<__bf16, NB, HB>(a, b, L, k + 1, wave, lane, idle);
+      // Tile k+1 goes into tile k-1's buffer once every wave is done with it, before this
+      // wave waits for tile k: two tiles in flight during the wait.
+      if (k + 1 < te) {
+        if (k > ta) lds_barrier();
+        issue_tile_dma<__bf16, NB, HB>(a, b, L, k + 1, wave, lane, idle);
+      }
+      wait_tile<2, G::kLoadsQ, G::kLoadsR>(k + 1 < te ? 1 : 0, wave);  // this wave's part of tile k landed
+      lds_barrier();  // every wave's part of tile k landed
 
       // S^T for tokens 16*mb + n16 (A rows) and this wave's 16 heads.
       // K step st = 4u + v reads chunk qk_c0/8 + 16u + ((4v + g) ^ sw) of row 16*mb + n16: the
