@@ -25,7 +25,8 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["Workload", "CONFIGS", "make_inputs", "DecodeInputs", "draw_lengths", "make_absorption_inputs"]
+__all__ = ["Workload", "CONFIGS", "make_inputs", "DecodeInputs", "draw_lengths", "make_absorption_inputs",
+           "GqaWorkload", "GQA_CONFIGS", "GqaInputs", "make_gqa_inputs"]
 
 D_ROPE = 64
 D_V = 128
@@ -274,3 +275,133 @@ def make_absorption_inputs(w: Workload, seed: int, B: int, *, shared_query: bool
         q = _randn(gen, (B, w.h, w.NB, D_NOPE), 1.0, w.torch_dtype)
     W_UK = _randn(gen, (w.NB, w.h, w.DL, D_NOPE), 1.0 / math.sqrt(D_NOPE), torch.float32)
     return q, W_UK
+
+
+# ---------------------------------------------------------------------------- GQA comparator
+#
+# Grouped-query attention at the shape the MLRA paper analyses it with (ai.info summary,
+# "Methodology in Plain English", 4th paragraph: 64 query heads, 8 KV heads, head dim 128):
+# the baseline MLRA-4's decode kernel is compared against ("Key Contributions" #4).
+# Draw order: lengths -> page-pool permutation -> q -> K cache -> V cache, all N(0, 1).
+
+
+@dataclasses.dataclass(frozen=True)
+class GqaWorkload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    lengths: tuple
+    page_size: int = 0
+    D: int = 128
+    dtype: str = "bf16"
+    sm_scale: float = 1.0 / math.sqrt(128.0)
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+    @property
+    def elem_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    @property
+    def token_elems(self) -> int:
+        """Cached elements per token: K and V of every KV head (2048 at H_kv = 8, D = 128)."""
+        return 2 * self.Hkv * self.D
+
+    def replace(self, **kw) -> "GqaWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+GQA_CONFIGS = {
+    "gqa_bf16_b32_hq64_hkv8_L32k": GqaWorkload("gqa_bf16_b32_hq64_hkv8_L32k", B=32, Hq=64, Hkv=8,
+                                               lengths=("fixed", 32768)),
+}
+
+
+@dataclasses.dataclass
+class GqaInputs:
+    """q [B, Hq, D], k_cache / v_cache [rows, Hkv, D], seqlens [B] int32, block_table or None."""
+
+    w: GqaWorkload
+    seqlens: torch.Tensor
+    max_seqlen: int
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    block_table: Optional[torch.Tensor] = None
+    max_pages: int = 0
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.seqlens.sum())
+
+    def to(self, device) -> "GqaInputs":
+        mv = lambda t: None if t is None else t.to(device)
+        return dataclasses.replace(self, seqlens=mv(self.seqlens), q=mv(self.q), k_cache=mv(self.k_cache),
+                                   v_cache=mv(self.v_cache), block_table=mv(self.block_table))
+
+    def cache_bytes(self) -> int:
+        return self.total_tokens * self.w.token_elems * self.w.elem_bytes
+
+
+def make_gqa_inputs(w: GqaWorkload, seed: int, *, lengths: Optional[Sequence[int]] = None,
+                    poison: bool = False, max_seqlen: Optional[int] = None, zero_q: bool = False,
+                    device: str = "cpu") -> GqaInputs:
+    """Draw one GQA workload. Lengths and the page permutation always come from a CPU
+    generator seeded with `seed`; q, K and V come from the same generator on the CPU, or,
+    with device="cuda", from a CUDA generator seeded with 1000 * seed + 29 (a different but
+    equally fixed stream, for full-size inputs that are slow to draw on the host)."""
+    gen = torch.Generator().manual_seed(int(seed))
+    Ls = draw_lengths(w, gen)
+    if lengths is not None:
+        Ls = [int(x) for x in lengths]
+    B, Hq, Hkv, D = len(Ls), w.Hq, w.Hkv, w.D
+    seqlens = torch.tensor(Ls, dtype=torch.int32)
+    msl = max(1, max(Ls) if Ls else 1) if max_seqlen is None else int(max_seqlen)
+    assert all(L <= msl for L in Ls)
+    block_table = None
+    max_pages = 0
+    if w.page_size:
+        P = w.page_size
+        pages_per_seq = [(L + P - 1) // P for L in Ls]
+        pool = sum(pages_per_seq)
+        perm = torch.randperm(max(pool, 1), generator=gen)[:pool]
+        max_pages = max(1, (msl + P - 1) // P)
+        block_table = torch.full((B, max_pages), -1, dtype=torch.int32)
+        off = 0
+        for b, n in enumerate(pages_per_seq):
+            block_table[b, :n] = perm[off:off + n].to(torch.int32)
+            off += n
+        rows = max(pool, 1) * P
+    else:
+        rows = B * msl
+    if device == "cpu":
+        tg, dev = gen, None
+    else:
+        tg, dev = torch.Generator(device=device).manual_seed(1000 * int(seed) + 29), device
+    draw = lambda shape: torch.randn(*shape, generator=tg, dtype=torch.float32, device=dev).to(w.torch_dtype)
+    q = draw((B, Hq, D))
+    if zero_q:
+        q.zero_()
+    k_cache = draw((rows, Hkv, D))
+    v_cache = draw((rows, Hkv, D))
+    if poison:
+        owned = torch.zeros(rows, dtype=torch.bool)
+        for b, L in enumerate(Ls):
+            if w.page_size:
+                P = w.page_size
+                t = torch.arange(L)
+                owned[block_table[b, (t // P)].long() * P + (t % P)] = True
+            else:
+                owned[b * msl: b * msl + L] = True
+        bad = (~owned).to(k_cache.device)
+        k_cache[bad] = float("nan")
+        v_cache[bad] = float("nan")
+    return GqaInputs(w=w, seqlens=seqlens, max_seqlen=msl, q=q, k_cache=k_cache, v_cache=v_cache,
+                     block_table=block_table, max_pages=max_pages)
