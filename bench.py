@@ -45,6 +45,8 @@ def parse():
                          "benchmark into the per-launch HBM traffic record under profiles/")
     ap.add_argument("--absorb", action="store_true",
                     help="also time the query-side absorption kernel (q_nope = W_UK q_pre) on this workload")
+    ap.add_argument("--no-gqa", action="store_true",
+                    help="skip the GQA comparator leg (64 query / 8 KV heads, d 128, same B and lengths)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step recorded once as a HIP graph and replayed (reported beside)")
     return ap.parse_args()
@@ -120,6 +122,33 @@ def record_traffic(fetch_csv, write_csv, args):
     out = os.path.join(ROOT, "profiles", f"traffic_decode_{w.name}.json")
     json.dump(rec, open(out, "w"), indent=1)
     print(json.dumps(rec))
+
+
+def gqa_leg(mlra, inp, args, stream, mlra_ms):
+    """The GQA decode comparator at the pages' GQA shape (64 query heads over 8 KV heads of
+    128 channels) on the same batch and lengths as the MLRA workload; inputs drawn on the GPU."""
+    import torch
+    from mlra_workloads import GQA_CONFIGS, make_gqa_inputs
+    g = GQA_CONFIGS["gqa_bf16_b32_hq64_hkv8_L32k"].replace(B=len(inp.seqlens), lengths=("list", tuple(inp.seqlens.tolist())))
+    gi = make_gqa_inputs(g, seed=args.config, device="cuda")
+    sl = gi.seqlens.to("cuda")
+    dec = mlra.GqaDecoder(gi.q, gi.k_cache, gi.v_cache, seqlens=sl, sm_scale=g.sm_scale, max_seqlen=gi.max_seqlen)
+    for _ in range(args.warmup):
+        dec(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dec(stream)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / args.steps
+    cb = gi.cache_bytes()
+    del dec, gi
+    torch.cuda.empty_cache()
+    return {"workload": f"gqa_bf16_b{g.B}_hq64_hkv8_d128 (lengths of this run)", "us_per_step": round(us, 2),
+            "cache_bytes": cb, "cache_GBps": round(cb / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(cb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "gqa_over_mlra_step_time": round(us / (mlra_ms * 1e3), 3),
+            "timing": "eager launches (attention + merge), K steps between two device synchronisations"}
 
 
 def cpu_baseline(inp, target_s):
@@ -285,6 +314,9 @@ def main():
         a_bytes = q_pre.numel() * q_pre.element_size() + W_UK.numel() * 4 + qn.numel() * qn.element_size()
         absorb = {"us_per_call": round(a_us, 2), "algorithmic_bytes": a_bytes,
                   "achieved_GBps": round(a_bytes / (a_us * 1e-6) / 1e9, 1)}
+    gqa = None
+    if not args.no_gqa and w.dtype == "bf16" and w.page_size == 0:
+        gqa = gqa_leg(mlra, inp, args, stream, ms_per_step)
     dk = sorted(e[0].elapsed_time(e[1]) for e in evs)
 
     ab = algorithmic_bytes(inp)
@@ -326,6 +358,7 @@ def main():
         "read_probe_GBps": None if read_gbps is None else round(read_gbps, 1),
         "roofline": roofline,
         "absorb_query": absorb,
+        "gqa_comparator": gqa,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

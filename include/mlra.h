@@ -186,6 +186,62 @@ int mlra_copy_bandwidth_probe(const void* src, void* dst, size_t bytes, void* st
  * caller-initialised), so the reads cannot be dropped. */
 int mlra_read_bandwidth_probe(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * Grouped-query (GQA) decode attention: the comparator the MLRA paper measures its decode
+ * kernel against ("Key Contributions" #4), at the shape it analyses GQA with (64 query heads,
+ * 8 KV heads, head dimension 128; "Methodology in Plain English", 4th paragraph). The pages
+ * do not define GQA; the standard form is built: query heads are cut into H_kv consecutive
+ * groups of G = H_q / H_kv, and for sequence b with L = seqlens[b] tokens, query head i:
+ *
+ *   g        = i / G
+ *   s_t      = sm_scale * <q[b,i,:], k_cache[t,g,:]>
+ *   out[b,i] = sum_t softmax_t(s) * v_cache[t,g,:]
+ *
+ * Same split-KV scheme, page table rules, stream and ownership rules as mlra_decode.
+ */
+typedef struct mlra_gqa_params {
+  int32_t batch;             /* B >= 0 */
+  int32_t num_q_heads;       /* H_q >= 1, a multiple of num_kv_heads, H_q / H_kv <= 16 */
+  int32_t num_kv_heads;      /* H_kv >= 1 */
+  int32_t head_dim;          /* must be 128 */
+  int32_t dtype;             /* must be MLRA_BF16 (q, k_cache, v_cache); out is fp32 */
+  int32_t page_size;         /* as in mlra_decode_params */
+  int32_t max_seqlen;        /* as in mlra_decode_params */
+  int32_t max_pages_per_seq; /* as in mlra_decode_params */
+  int32_t num_splits;        /* token splits (each launched once per KV head); 0 = resident
+                                workgroup slots of the device / num_kv_heads */
+  int32_t reserved;          /* must be 0 */
+  int64_t q_stride_b, q_stride_h;       /* elements; the head_dim row is contiguous */
+  int64_t k_stride_tok, k_stride_head;  /* elements between cache rows / KV heads of k_cache */
+  int64_t v_stride_tok, v_stride_head;  /* same for v_cache */
+  float sm_scale;            /* > 0, e.g. 1/sqrt(128) */
+  float reserved_f;          /* must be 0 */
+} mlra_gqa_params;
+
+/* Host-only validation of `p`. Returns 0 or a negative code. */
+int mlra_gqa_check_params(const mlra_gqa_params* p);
+
+/* Token splits a GQA call with `p` uses (p->num_splits if positive). Returns 0 or a negative code. */
+int mlra_gqa_num_splits(const mlra_gqa_params* p, int32_t* num_splits);
+
+/* Bytes of workspace mlra_gqa_decode needs for `p`. */
+int mlra_gqa_workspace_size(const mlra_gqa_params* p, size_t* bytes);
+
+/*
+ * GQA decode step, two kernel launches on `stream`: the split-KV attention kernel (one
+ * single-wave workgroup per token split and KV head, per-query-head online softmax,
+ * partials in `workspace`) and the log-sum-exp merge into `out`.
+ *   q        [B][H_q] rows of head_dim elements (strides q_stride_b/h); bf16
+ *   k_cache  token t of sequence b, KV head g at row*k_stride_tok + g*k_stride_head, with
+ *            row numbered as in mlra_decode (contiguous: b*max_seqlen + t; paged: block
+ *            table); bf16. v_cache the same with the v strides.
+ *   out      fp32 [B][H_q][head_dim], contiguous; fully written
+ * Base pointers and strides 16-byte aligned; workspace 256-byte aligned.
+ */
+int mlra_gqa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                    const int32_t* seqlens, float* out, const mlra_gqa_params* p, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

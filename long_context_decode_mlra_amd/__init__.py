@@ -13,10 +13,12 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (MLRA_BF16, MLRA_F32, MLRA_MAX_HEADS, MLRA_TILE_TOKENS, DecodeParams, MlraError, check, lib)
+from ._lib import (MLRA_BF16, MLRA_F32, MLRA_MAX_HEADS, MLRA_TILE_TOKENS, DecodeParams, GqaParams, MlraError,
+                   check, lib)
 
 __all__ = ["decode", "decode_splitkv", "decode_combine", "make_params", "Decoder", "workspace_size", "num_splits",
-           "check_params", "plan", "copy_bandwidth_probe", "read_bandwidth_probe", "absorb_query", "MlraError", "DecodeParams", "MLRA_BF16", "MLRA_F32",
+           "check_params", "plan", "copy_bandwidth_probe", "read_bandwidth_probe", "absorb_query", "MlraError",
+           "DecodeParams", "GqaParams", "GqaDecoder", "gqa_decode", "make_gqa_params", "MLRA_BF16", "MLRA_F32",
            "MLRA_TILE_TOKENS", "MLRA_MAX_HEADS", "lib"]
 
 _DTYPES = {torch.bfloat16: MLRA_BF16, torch.float32: MLRA_F32}
@@ -194,3 +196,62 @@ def absorb_query(q_pre: torch.Tensor, W_UK: torch.Tensor, q_nope: torch.Tensor, 
     check(lib().mlra_absorb_query(_ptr(q_pre), _ptr(W_UK), _ptr(q_nope), ctypes.byref(p), q_pre.shape[3],
                                   q_pre.stride(0), q_pre.stride(1), q_pre.stride(2), _stream(stream)))
     return q_nope
+
+
+# ---------------------------------------------------------------------------- GQA comparator
+
+def make_gqa_params(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, *, sm_scale: float,
+                    max_seqlen: int, page_size: int = 0, max_pages_per_seq: int = 0,
+                    num_splits: int = 0) -> GqaParams:
+    """q [B, H_q, 128], k_cache / v_cache [rows, H_kv, 128] (bf16; innermost rows contiguous)."""
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[1]
+    if any(t.dtype != torch.bfloat16 for t in (q, k_cache, v_cache)):
+        raise ValueError("q, k_cache and v_cache must be bfloat16")
+    if q.stride(2) != 1 or k_cache.stride(2) != 1 or v_cache.stride(2) != 1 or v_cache.shape[1] != Hkv:
+        raise ValueError("q, k_cache and v_cache need contiguous head rows and matching KV heads")
+    p = GqaParams()
+    p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.dtype = B, Hq, Hkv, D, MLRA_BF16
+    p.page_size, p.max_seqlen, p.max_pages_per_seq, p.num_splits, p.reserved = \
+        page_size, max_seqlen, max_pages_per_seq, num_splits, 0
+    p.q_stride_b, p.q_stride_h = q.stride(0), q.stride(1)
+    p.k_stride_tok, p.k_stride_head = k_cache.stride(0), k_cache.stride(1)
+    p.v_stride_tok, p.v_stride_head = v_cache.stride(0), v_cache.stride(1)
+    p.sm_scale, p.reserved_f = sm_scale, 0.0
+    return p
+
+
+class GqaDecoder:
+    """One GQA decode configuration with its workspace and output, for repeated calls."""
+
+    def __init__(self, q, k_cache, v_cache, *, seqlens, sm_scale, max_seqlen, block_table=None, page_size=0,
+                 num_splits=0):
+        maxp = 0 if block_table is None else block_table.shape[1]
+        self.p = make_gqa_params(q, k_cache, v_cache, sm_scale=sm_scale, max_seqlen=max_seqlen,
+                                 page_size=page_size, max_pages_per_seq=maxp, num_splits=num_splits)
+        for t, name in ((seqlens, "seqlens"), (block_table, "block_table")):
+            if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+                raise ValueError(f"{name} must be a contiguous int32 tensor")
+        check(lib().mlra_gqa_check_params(ctypes.byref(self.p)))
+        self.tensors = (q, k_cache, v_cache, block_table, seqlens)
+        self.out = torch.empty(q.shape[0], q.shape[1], q.shape[2], dtype=torch.float32, device=q.device)
+        n = ctypes.c_size_t(0)
+        check(lib().mlra_gqa_workspace_size(ctypes.byref(self.p), ctypes.byref(n)))
+        self.ws_bytes = n.value
+        self.workspace = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=q.device)
+        g = ctypes.c_int32(0)
+        check(lib().mlra_gqa_num_splits(ctypes.byref(self.p), ctypes.byref(g)))
+        self.splits = g.value
+
+    def __call__(self, stream=None) -> torch.Tensor:
+        q, k, v, bt, sl = self.tensors
+        check(lib().mlra_gqa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(bt), _ptr(sl), _ptr(self.out),
+                                    ctypes.byref(self.p), _ptr(self.workspace), self.ws_bytes, _stream(stream)))
+        return self.out
+
+
+def gqa_decode(q, k_cache, v_cache, seqlens, *, sm_scale: float, max_seqlen: int, block_table=None,
+               page_size: int = 0, num_splits: int = 0, stream=None) -> torch.Tensor:
+    """out[b, i] = softmax_t(sm_scale <q[b,i], K[t, g]>) V[t, g], g = i // (H_q / H_kv)."""
+    return GqaDecoder(q, k_cache, v_cache, seqlens=seqlens, sm_scale=sm_scale, max_seqlen=max_seqlen,
+                      block_table=block_table, page_size=page_size, num_splits=num_splits)(stream)

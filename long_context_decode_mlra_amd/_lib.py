@@ -18,7 +18,8 @@ ERRORS = {0: "MLRA_OK", -1: "MLRA_ERR_NULL", -2: "MLRA_ERR_SHAPE", -3: "MLRA_ERR
 # Every symbol include/mlra.h declares.
 EXPORTS = ("mlra_abi_version", "mlra_last_error", "mlra_check_params", "mlra_decode_num_splits",
            "mlra_decode_workspace_size", "mlra_decode", "mlra_decode_splitkv", "mlra_decode_combine",
-           "mlra_decode_plan", "mlra_copy_bandwidth_probe", "mlra_read_bandwidth_probe", "mlra_absorb_query")
+           "mlra_decode_plan", "mlra_copy_bandwidth_probe", "mlra_read_bandwidth_probe", "mlra_absorb_query",
+           "mlra_gqa_check_params", "mlra_gqa_num_splits", "mlra_gqa_workspace_size", "mlra_gqa_decode")
 
 
 class DecodeParams(ctypes.Structure):
@@ -31,6 +32,19 @@ class DecodeParams(ctypes.Structure):
         ("qr_stride_b", ctypes.c_int64), ("qr_stride_h", ctypes.c_int64),
         ("lat_stride_tok", ctypes.c_int64), ("rope_stride_tok", ctypes.c_int64),
         ("sm_scale", ctypes.c_float), ("out_scale", ctypes.c_float),
+    ]
+
+
+class GqaParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("max_seqlen", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("q_stride_b", ctypes.c_int64), ("q_stride_h", ctypes.c_int64),
+        ("k_stride_tok", ctypes.c_int64), ("k_stride_head", ctypes.c_int64),
+        ("v_stride_tok", ctypes.c_int64), ("v_stride_head", ctypes.c_int64),
+        ("sm_scale", ctypes.c_float), ("reserved_f", ctypes.c_float),
     ]
 
 
@@ -66,6 +80,11 @@ def lib() -> ctypes.CDLL:
     L.mlra_read_bandwidth_probe.argtypes = [vp, sz, vp, vp]
     i64 = ctypes.c_int64
     L.mlra_absorb_query.argtypes = [vp, vp, vp, P, i32, i64, i64, i64, vp]
+    GP = ctypes.POINTER(GqaParams)
+    L.mlra_gqa_check_params.argtypes = [GP]
+    L.mlra_gqa_num_splits.argtypes = [GP, ctypes.POINTER(i32)]
+    L.mlra_gqa_workspace_size.argtypes = [GP, ctypes.POINTER(sz)]
+    L.mlra_gqa_decode.argtypes = [vp, vp, vp, vp, vp, vp, GP, vp, sz, vp]
     for name in EXPORTS:
         if name not in ("mlra_last_error", "mlra_abi_version"):
             getattr(L, name).restype = ctypes.c_int

@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libmlra.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 # HIP translation units of the library, compiled in parallel.
-HIP_SOURCES = ("mlra_attention.hip", "mlra_combine.hip", "mlra_absorb.hip", "mlra_probes.hip")
+HIP_SOURCES = ("mlra_attention.hip", "mlra_combine.hip", "mlra_absorb.hip", "mlra_probes.hip",
+               "gqa_attention.hip")
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are kept out of every kernel.

@@ -45,6 +45,21 @@ int head_blocks(int num_heads);
 
 bool aligned16(const void* ptr);
 
+// GQA comparator workspace: part_o fp32 [slots][H_q][128], part_ml fp32 [slots][H_q][2],
+// prefix int64 [B + 3]; slots = G + B.
+struct GqaLayout {
+  int64_t slots = 0;
+  size_t part_o_off = 0;
+  size_t part_ml_off = 0;
+  size_t prefix_off = 0;
+  size_t total = 0;
+};
+constexpr int kGqaHeadDim = 128;
+constexpr int kGqaMaxGroup = 16;
+GqaLayout gqa_layout(const mlra_gqa_params& p, int32_t num_splits);
+int gqa_prepare(const mlra_gqa_params* p, const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+                int32_t* G, GqaLayout* lay);
+
 // Validates p, resolves the split count G and the workspace layout, and checks the
 // workspace pointer and size (B = 0 needs neither seqlens nor a workspace).
 int prepare(const mlra_decode_params* p, const int32_t* seqlens, void* workspace, size_t workspace_bytes,

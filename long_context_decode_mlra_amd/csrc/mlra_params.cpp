@@ -62,6 +62,33 @@ int prepare(const mlra_decode_params* p, const int32_t* seqlens, void* workspace
   return MLRA_OK;
 }
 
+GqaLayout gqa_layout(const mlra_gqa_params& p, int32_t num_splits) {
+  GqaLayout w;
+  w.slots = int64_t(num_splits) + int64_t(p.batch);
+  w.part_o_off = 0;
+  w.part_ml_off = align256(size_t(w.slots) * size_t(p.num_q_heads) * kGqaHeadDim * sizeof(float));
+  w.prefix_off = align256(w.part_ml_off + size_t(w.slots) * size_t(p.num_q_heads) * 2 * sizeof(float));
+  w.total = align256(w.prefix_off + (size_t(p.batch) + 3) * sizeof(int64_t));
+  return w;
+}
+
+int gqa_prepare(const mlra_gqa_params* p, const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+                int32_t* G, GqaLayout* lay) {
+  int rc = mlra_gqa_check_params(p);
+  if (rc) return rc;
+  rc = mlra_gqa_num_splits(p, G);
+  if (rc) return rc;
+  *lay = gqa_layout(*p, *G);
+  if (p->batch == 0) return MLRA_OK;
+  if (!seqlens) return set_error(MLRA_ERR_NULL, "seqlens is NULL");
+  if (!workspace) return set_error(MLRA_ERR_WORKSPACE, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return set_error(MLRA_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (workspace_bytes < lay->total)
+    return set_error(MLRA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, lay->total);
+  return MLRA_OK;
+}
+
 }  // namespace mlra
 
 using namespace mlra;
@@ -116,5 +143,47 @@ extern "C" int mlra_check_params(const mlra_decode_params* p) {
   if (!(std::isfinite(p->sm_scale) && p->sm_scale > 0.f))
     return set_error(MLRA_ERR_SHAPE, "sm_scale must be finite and > 0");
   if (!std::isfinite(p->out_scale)) return set_error(MLRA_ERR_SHAPE, "out_scale must be finite");
+  return MLRA_OK;
+}
+
+extern "C" int mlra_gqa_check_params(const mlra_gqa_params* p) {
+  if (!p) return set_error(MLRA_ERR_NULL, "params pointer is NULL");
+  if (p->reserved != 0 || p->reserved_f != 0.f) return set_error(MLRA_ERR_SHAPE, "reserved fields must be 0");
+  if (p->batch < 0) return set_error(MLRA_ERR_SHAPE, "batch must be >= 0 (got %d)", p->batch);
+  if (p->num_kv_heads < 1 || p->num_q_heads < 1 || p->num_q_heads % p->num_kv_heads != 0)
+    return set_error(MLRA_ERR_SHAPE, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                     p->num_q_heads, p->num_kv_heads);
+  if (p->num_q_heads / p->num_kv_heads > kGqaMaxGroup)
+    return set_error(MLRA_ERR_UNSUPPORTED, "at most %d query heads per KV head (got %d)", kGqaMaxGroup,
+                     p->num_q_heads / p->num_kv_heads);
+  if (p->head_dim != kGqaHeadDim)
+    return set_error(MLRA_ERR_UNSUPPORTED, "head_dim must be %d (got %d)", kGqaHeadDim, p->head_dim);
+  if (p->dtype != MLRA_BF16) return set_error(MLRA_ERR_UNSUPPORTED, "the GQA decode takes bf16 only");
+  if (p->max_seqlen < 0) return set_error(MLRA_ERR_SHAPE, "max_seqlen must be >= 0 (got %d)", p->max_seqlen);
+  if (p->page_size < 0) return set_error(MLRA_ERR_SHAPE, "page_size must be >= 0 (got %d)", p->page_size);
+  if (p->page_size > 0) {
+    if (p->page_size % kTile != 0)
+      return set_error(MLRA_ERR_UNSUPPORTED, "page_size must be a multiple of %d (got %d)", kTile, p->page_size);
+    const int64_t need = (int64_t(p->max_seqlen) + p->page_size - 1) / p->page_size;
+    if (p->max_pages_per_seq < need)
+      return set_error(MLRA_ERR_SHAPE, "max_pages_per_seq %d < ceil(max_seqlen / page_size) = %lld",
+                       p->max_pages_per_seq, (long long)need);
+  }
+  if (p->num_splits < 0) return set_error(MLRA_ERR_SHAPE, "num_splits must be >= 0 (got %d)", p->num_splits);
+  if (p->q_stride_h < kGqaHeadDim || p->q_stride_b < 0)
+    return set_error(MLRA_ERR_SHAPE, "query strides too small (q_stride_h %lld)", (long long)p->q_stride_h);
+  if (p->k_stride_tok < 0 || p->k_stride_head < 0 || p->v_stride_tok < 0 || p->v_stride_head < 0)
+    return set_error(MLRA_ERR_SHAPE, "cache strides must be >= 0");
+  // Rows of one 32-token tile are addressed with 32-bit offsets.
+  if (p->k_stride_tok * 2 * kTile > (int64_t(1) << 30) || p->v_stride_tok * 2 * kTile > (int64_t(1) << 30))
+    return set_error(MLRA_ERR_SHAPE, "cache row stride too large");
+  const int64_t strides[6] = {p->q_stride_b, p->q_stride_h, p->k_stride_tok, p->k_stride_head,
+                              p->v_stride_tok, p->v_stride_head};
+  for (int k = 0; k < 6; ++k)
+    if ((strides[k] * 2) % 16 != 0)
+      return set_error(MLRA_ERR_ALIGN, "stride #%d (%lld elements) is not a multiple of 16 bytes", k,
+                       (long long)strides[k]);
+  if (!(std::isfinite(p->sm_scale) && p->sm_scale > 0.f))
+    return set_error(MLRA_ERR_SHAPE, "sm_scale must be finite and > 0");
   return MLRA_OK;
 }

@@ -136,3 +136,63 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(L, "_lib", None)
     with pytest.raises(ImportError):
         L.lib()
+
+
+# ---------------------------------------------------------------------------- GQA comparator
+def good_gqa(**kw):
+    L = _lib()
+    p = L.GqaParams()
+    p.batch, p.num_q_heads, p.num_kv_heads, p.head_dim, p.dtype = 32, 64, 8, 128, 0
+    p.page_size, p.max_seqlen, p.max_pages_per_seq, p.num_splits, p.reserved = 0, 32768, 0, 96, 0
+    p.q_stride_b, p.q_stride_h = 64 * 128, 128
+    p.k_stride_tok, p.k_stride_head, p.v_stride_tok, p.v_stride_head = 8 * 128, 128, 8 * 128, 128
+    p.sm_scale, p.reserved_f = 1 / math.sqrt(128), 0.0
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def gqa_rc(p):
+    return _lib().lib().mlra_gqa_check_params(ctypes.byref(p))
+
+
+def test_gqa_valid_params_pass():
+    assert gqa_rc(good_gqa()) == 0
+    assert gqa_rc(good_gqa(num_q_heads=16, num_kv_heads=1)) == 0
+    assert gqa_rc(good_gqa(page_size=64, max_pages_per_seq=512)) == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("batch", -1, -2), ("num_kv_heads", 0, -2), ("num_q_heads", 60, -2), ("num_q_heads", 136, -3),
+    ("head_dim", 64, -3), ("dtype", 1, -3), ("max_seqlen", -1, -2), ("page_size", 48, -3),
+    ("page_size", 64, -2), ("num_splits", -1, -2), ("reserved", 1, -2), ("reserved_f", 1.0, -2),
+    ("q_stride_h", 64, -2), ("k_stride_tok", -8, -2), ("v_stride_head", 100, -4), ("q_stride_b", 8 * 128 + 4, -4),
+    ("k_stride_tok", 1 << 25, -2), ("sm_scale", 0.0, -2), ("sm_scale", float("inf"), -2),
+])
+def test_gqa_bad_params_rejected(field, value, code):
+    assert gqa_rc(good_gqa(**{field: value})) == code
+
+
+def test_gqa_workspace_size_with_explicit_splits_needs_no_device():
+    L = _lib()
+    p = good_gqa(num_splits=96)
+    n = ctypes.c_size_t(0)
+    assert L.lib().mlra_gqa_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    slots = 96 + 32
+    expect = slots * 64 * 128 * 4 + slots * 64 * 2 * 4 + 35 * 8
+    assert n.value >= expect and n.value % 256 == 0 and n.value < expect + 3 * 256
+
+
+def test_gqa_argument_errors_before_any_launch():
+    L = _lib()
+    lib = L.lib()
+    p = good_gqa(num_splits=8)
+    fake = ctypes.c_void_p(1 << 20)
+    n = ctypes.c_size_t(0)
+    lib.mlra_gqa_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    assert lib.mlra_gqa_decode(fake, fake, fake, None, fake, fake, ctypes.byref(p), fake, 256, None) == -5
+    assert lib.mlra_gqa_decode(None, fake, fake, None, fake, fake, ctypes.byref(p), fake, n.value, None) == -1
+    assert lib.mlra_gqa_decode(fake, ctypes.c_void_p((1 << 20) + 8), fake, None, fake, fake, ctypes.byref(p), fake,
+                               n.value, None) == -4
+    assert lib.mlra_gqa_decode(fake, fake, fake, fake, fake, fake, ctypes.byref(p), fake, n.value, None) == -1
+    assert lib.mlra_gqa_decode(fake, fake, fake, None, None, fake, ctypes.byref(p), fake, n.value, None) == -1
