@@ -32,7 +32,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50,
+                    help="untimed steps first (a fresh GPU needs a few dozen launches to reach steady clocks)")
     ap.add_argument("--config", type=int, default=2, help="workload number (1-5); 2 is the headline")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = one split per resident workgroup slot")
     ap.add_argument("--no-cpu-baseline", action="store_true")

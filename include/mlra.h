@@ -78,7 +78,9 @@ typedef struct mlra_decode_params {
                                 block_table required, tokens per page, a multiple of 32 */
   int32_t max_seqlen;        /* >= every seqlens[b]; contiguous cache: rows reserved per sequence */
   int32_t max_pages_per_seq; /* paged cache: row stride of block_table (>= ceil(max_seqlen/page_size)) */
-  int32_t num_splits;        /* decode workgroups; 0 = one per resident slot on the device */
+  int32_t num_splits;        /* decode workgroups, one split each; 0 = one per resident slot on the
+                                device, and then, when the batch's tiles would give fewer than 56
+                                per split, the kernel runs one split per compute unit instead */
   int32_t reserved;          /* must be 0 */
   int64_t q_stride_b, q_stride_h;   /* q_nope strides in elements; the NB*d_latent row is contiguous */
   int64_t qr_stride_b, qr_stride_h; /* q_rope strides in elements; the d_rope row is contiguous */

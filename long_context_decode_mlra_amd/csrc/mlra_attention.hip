@@ -79,6 +79,13 @@ constexpr float kRescaleSlack = 8.0f;
 // The asm statement is also a compiler memory barrier.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Splits shorter than this many tiles pay their fixed costs (query loads, one 64 KiB
+// partial per sequence touched, the combine's share) on too few cache bytes: below it, with
+// two resident workgroups per compute unit, one split per unit streams as fast and halves
+// the partials. Measured on MI355X: B=4 L=64K-128K (24 tiles per split at 512 splits) and
+// B=64 L=1K-64K (48) run faster with 256 splits, B=32 L=32K (64) with 512.
+constexpr int kMinTilesPerSplit = 56;
+
 struct DecodeArgs {
   const unsigned char* q_nope;
   const unsigned char* q_rope;
@@ -90,10 +97,20 @@ struct DecodeArgs {
   float* part_ml;
   int64_t* prefix;  // [B + 3]: first global tile of each sequence, then T, T, G (written by workgroup 0)
   int B, h, G_req, page_size, max_seqlen, max_pages;
+  int G_small;                       // > 0: use this many splits when splits would be short (see split_plan)
   int64_t q_sb, q_sh, qr_sb, qr_sh;  // bytes
   int64_t lat_stride, rope_stride;   // bytes
   float c;                           // sm_scale * log2(e)
 };
+
+// The split plan of a launch of G_req workgroups, switched to G_small splits when the tiles
+// would give fewer than kMinTilesPerSplit per split. Workgroups g >= G exit at once; the first
+// G_small of them land one per compute unit (workgroups are dealt round-robin over the XCDs).
+__device__ __forceinline__ Plan split_plan(const DecodeArgs& a) {
+  Plan p = make_plan(a.seqlens, a.B, a.G_req);
+  if (a.G_small > 0 && p.T < int64_t(kMinTilesPerSplit) * a.G_req) p.G = int(p.T < a.G_small ? p.T : a.G_small);
+  return p;
+}
 
 // Tile geometry. The LDS copy of a tile keeps the cache row order; within each row the
 // 16-byte chunk c of token t sits at chunk position c ^ lat_swizzle(t) (latent rows) or
@@ -384,7 +401,7 @@ void decode_kernel(DecodeArgs a) {
   const int head = hb * kHeadBlock + n;
   const bool head_ok = head < a.h;
 
-  const Plan plan = make_plan(a.seqlens, a.B, a.G_req);
+  const Plan plan = split_plan(a);
   const int g = blockIdx.x;
   if (g == 0 && wave == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
   if (g >= plan.G) return;
@@ -556,7 +573,7 @@ void decode_hs_kernel(DecodeArgs a) {
   const int head = 16 * hq + n16;
   const bool head_ok = head < a.h;
 
-  const Plan plan = make_plan(a.seqlens, a.B, a.G_req);
+  const Plan plan = split_plan(a);
   const int gsplit = blockIdx.x;
   if (gsplit == 0 && wave == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
   if (gsplit >= plan.G) return;
@@ -748,10 +765,12 @@ DecodeFn pick_decode(int dtype, int nb, int hb) {
   return nullptr;
 }
 
-// Resident decode workgroups per device, cached per (device, kernel).
-int resident_splits(const mlra_decode_params& p, int32_t* out) {
+// Resident decode workgroups per device, cached per (device, kernel); *cus_out (optional)
+// receives the compute units of the device.
+int resident_splits(const mlra_decode_params& p, int32_t* out, int* cus_out = nullptr) {
   static std::mutex mu;
   static int cache[64][2][3][2];  // device, dtype, log2 NB, HB-1
+  static int cus_cache[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -761,6 +780,7 @@ int resident_splits(const mlra_decode_params& p, int32_t* out) {
     std::lock_guard<std::mutex> lk(mu);
     if (cache[dev][p.dtype][nbi][hb - 1] > 0) {
       *out = cache[dev][p.dtype][nbi][hb - 1];
+      if (cus_out) *cus_out = cus_cache[dev];
       return MLRA_OK;
     }
   }
@@ -776,8 +796,10 @@ int resident_splits(const mlra_decode_params& p, int32_t* out) {
   if (dev >= 0 && dev < 64) {
     std::lock_guard<std::mutex> lk(mu);
     cache[dev][p.dtype][nbi][hb - 1] = n;
+    cus_cache[dev] = cus;
   }
   *out = n;
+  if (cus_out) *cus_out = cus;
   return MLRA_OK;
 }
 
@@ -836,6 +858,15 @@ extern "C" int mlra_decode_splitkv(const void* q_nope, const void* q_rope, const
   a.B = p->batch;
   a.h = p->num_heads;
   a.G_req = G;
+  a.G_small = 0;
+  if (p->num_splits == 0) {
+    // Default split count: allow one split per compute unit instead of two for short splits.
+    int32_t resident = 0;
+    int cus = 0;
+    rc = resident_splits(*p, &resident, &cus);
+    if (rc) return rc;
+    if (cus > 0 && G >= 2 * cus) a.G_small = cus;
+  }
   a.page_size = p->page_size > 0 ? p->page_size : 1;
   a.max_seqlen = p->max_seqlen;
   a.max_pages = p->max_pages_per_seq;
