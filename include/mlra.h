@@ -153,8 +153,9 @@ int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, float* out, c
  *     q_nope[b,i,j,:] = W_UK[j,i] @ q_pre[b,i,j,:]      (d_latent x d_nope times d_nope)
  * turns the NoPE query of each head into latent coordinates, the input mlra_decode takes.
  *   q_pre   [B][h][NB] rows of d_nope = 128 elements (dtype), strides qpre_stride_b/h/j in
- *           elements; qpre_stride_j = 0 shares one NoPE query across the latent heads
- *   W_UK    fp32 [NB][h][d_latent][d_nope], contiguous (row = latent channel)
+ *           elements; qpre_stride_j = 0 shares one NoPE query across the latent heads.
+ *           Base pointer and strides 16-byte aligned (MLRA_ERR_ALIGN otherwise)
+ *   W_UK    fp32 [NB][h][d_latent][d_nope], contiguous (row = latent channel), 16-byte aligned
  *   q_nope  output, dtype, laid out as mlra_decode reads it (p->q_stride_b, p->q_stride_h;
  *           latent head j at offset j*d_latent); rounded to nearest (even) for bf16
  * One kernel launch on `stream`. Returns 0 or a negative code.

@@ -17,7 +17,7 @@ from ._lib import (MLRA_BF16, MLRA_F32, MLRA_MAX_HEADS, MLRA_TILE_TOKENS, Decode
                    check, lib)
 
 __all__ = ["decode", "decode_splitkv", "decode_combine", "make_params", "Decoder", "workspace_size", "num_splits",
-           "check_params", "plan", "copy_bandwidth_probe", "read_bandwidth_probe", "absorb_query", "MlraError",
+           "check_params", "plan", "copy_bandwidth_probe", "read_bandwidth_probe", "absorb_query", "Absorber", "MlraError",
            "DecodeParams", "GqaParams", "GqaDecoder", "gqa_decode", "make_gqa_params", "MLRA_BF16", "MLRA_F32",
            "MLRA_TILE_TOKENS", "MLRA_MAX_HEADS", "lib"]
 
@@ -175,27 +175,40 @@ def read_bandwidth_probe(src: torch.Tensor, sink: torch.Tensor, stream=None) -> 
     check(lib().mlra_read_bandwidth_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
 
 
+class Absorber:
+    """Decode step 1 for fixed tensors: q_nope[b, i, j, :] = W_UK[j, i] @ q_pre[b, i, j, :], written
+    into q_nope ([B, h, NB, d_latent], rows contiguous, the layout the decode takes). q_pre is
+    [B, h, NB, 128] (a stride-0 branch axis shares one query across latent heads). The C
+    arguments are built once; each call is one launch."""
+
+    def __init__(self, q_pre: torch.Tensor, W_UK: torch.Tensor, q_nope: torch.Tensor):
+        B, h, NB, DL = q_nope.shape
+        if q_pre.shape[:3] != (B, h, NB) or q_pre.stride(3) != 1 or q_pre.dtype != q_nope.dtype:
+            raise ValueError("q_pre must be [B, h, NB, d_nope] with contiguous rows and q_nope's dtype")
+        if W_UK.dtype != torch.float32 or not W_UK.is_contiguous() or tuple(W_UK.shape[:3]) != (NB, h, DL):
+            raise ValueError("W_UK must be a contiguous float32 tensor [NB, h, d_latent, d_nope]")
+        if q_nope.stride(3) != 1 or q_nope.stride(2) != DL:
+            raise ValueError("q_nope rows [NB, DL] must be contiguous")
+        p = DecodeParams()
+        p.batch, p.num_heads, p.num_branches, p.d_latent, p.d_rope, p.d_v = B, h, NB, DL, 64, 128
+        p.dtype = _DTYPES[q_nope.dtype]
+        p.q_stride_b, p.q_stride_h = q_nope.stride(0), q_nope.stride(1)
+        p.qr_stride_b, p.qr_stride_h = h * 64, 64
+        p.lat_stride_tok, p.rope_stride_tok = NB * DL, 64
+        p.sm_scale, p.out_scale = 1.0, 1.0
+        self.p, self.q_nope = p, q_nope
+        self.tensors = (q_pre, W_UK, q_nope)
+        self.args = (_ptr(q_pre), _ptr(W_UK), _ptr(q_nope), ctypes.byref(p), q_pre.shape[3], q_pre.stride(0),
+                     q_pre.stride(1), q_pre.stride(2))
+
+    def __call__(self, stream=None) -> torch.Tensor:
+        check(lib().mlra_absorb_query(*self.args, _stream(stream)))
+        return self.q_nope
+
+
 def absorb_query(q_pre: torch.Tensor, W_UK: torch.Tensor, q_nope: torch.Tensor, stream=None) -> torch.Tensor:
-    """Decode step 1: q_nope[b, i, j, :] = W_UK[j, i] @ q_pre[b, i, j, :], written into q_nope
-    ([B, h, NB, d_latent], rows contiguous, the layout the decode takes). q_pre is
-    [B, h, NB, 128] (a stride-0 branch axis shares one query across latent heads)."""
-    B, h, NB, DL = q_nope.shape
-    if q_pre.shape[:3] != (B, h, NB) or q_pre.stride(3) != 1 or q_pre.dtype != q_nope.dtype:
-        raise ValueError("q_pre must be [B, h, NB, d_nope] with contiguous rows and q_nope's dtype")
-    if W_UK.dtype != torch.float32 or not W_UK.is_contiguous() or tuple(W_UK.shape[:3]) != (NB, h, DL):
-        raise ValueError("W_UK must be a contiguous float32 tensor [NB, h, d_latent, d_nope]")
-    if q_nope.stride(3) != 1 or q_nope.stride(2) != DL:
-        raise ValueError("q_nope rows [NB, DL] must be contiguous")
-    p = DecodeParams()
-    p.batch, p.num_heads, p.num_branches, p.d_latent, p.d_rope, p.d_v = B, h, NB, DL, 64, 128
-    p.dtype = _DTYPES[q_nope.dtype]
-    p.q_stride_b, p.q_stride_h = q_nope.stride(0), q_nope.stride(1)
-    p.qr_stride_b, p.qr_stride_h = h * 64, 64
-    p.lat_stride_tok, p.rope_stride_tok = NB * DL, 64
-    p.sm_scale, p.out_scale = 1.0, 1.0
-    check(lib().mlra_absorb_query(_ptr(q_pre), _ptr(W_UK), _ptr(q_nope), ctypes.byref(p), q_pre.shape[3],
-                                  q_pre.stride(0), q_pre.stride(1), q_pre.stride(2), _stream(stream)))
-    return q_nope
+    """Decode step 1 (see Absorber): q_nope[b, i, j, :] = W_UK[j, i] @ q_pre[b, i, j, :]."""
+    return Absorber(q_pre, W_UK, q_nope)(stream)
 
 
 # ---------------------------------------------------------------------------- GQA comparator

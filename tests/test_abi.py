@@ -196,3 +196,19 @@ def test_gqa_argument_errors_before_any_launch():
                                n.value, None) == -4
     assert lib.mlra_gqa_decode(fake, fake, fake, fake, fake, fake, ctypes.byref(p), fake, n.value, None) == -1
     assert lib.mlra_gqa_decode(fake, fake, fake, None, None, fake, ctypes.byref(p), fake, n.value, None) == -1
+
+
+def test_absorb_argument_errors_before_any_launch():
+    L = _lib()
+    lib = L.lib()
+    p = good_params(num_splits=8)
+    fake = ctypes.c_void_p(1 << 20)
+    i64 = ctypes.c_int64
+    ok = (i64(32 * 4 * 128), i64(4 * 128), i64(128))
+    assert lib.mlra_absorb_query(fake, fake, fake, ctypes.byref(p), 64, *ok, None) == -3      # d_nope
+    assert lib.mlra_absorb_query(None, fake, fake, ctypes.byref(p), 128, *ok, None) == -1     # NULL q_pre
+    assert lib.mlra_absorb_query(ctypes.c_void_p((1 << 20) + 8), fake, fake, ctypes.byref(p), 128, *ok,
+                                 None) == -4                                                  # misaligned q_pre
+    assert lib.mlra_absorb_query(fake, fake, fake, ctypes.byref(p), 128, i64(32 * 4 * 128), i64(4 * 128),
+                                 i64(4), None) == -4                                          # 8-byte stride
+    assert lib.mlra_absorb_query(fake, fake, fake, ctypes.byref(p), 128, i64(-1), *ok[1:], None) == -2
