@@ -201,8 +201,8 @@ def test_full_size_sampled(cfg):
 
 
 def test_two_sequence_groups_and_workspace_reuse():
-    """B=40: one full group of 32 sequences and a partial one; the same Decoder (workspace,
-    arrival counters) is called three times in a row and must give the same bits."""
+    """B=40: one full group of 32 sequences and a partial one; the same Decoder (and workspace)
+    is called three times in a row and must give the same bits."""
     mlra = _mlra()
     rng = np.random.default_rng(40)
     Ls = tuple(int(x) for x in rng.integers(0, 900, size=40))
@@ -218,6 +218,28 @@ def test_two_sequence_groups_and_workspace_reuse():
     ref = oracle.decode_inputs(inp)
     assert_parity(outs[0], ref, label="B=40")
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_one_sequence_of_a_million_tokens():
+    """Maximum length on one GPU-resident sequence: B=1, L=2^20 (1.2 GB of cache). Every split
+    of the default launch falls in the same sequence, so the combine merges 512+1 slots for it."""
+    w = CONFIGS[2].replace(B=1, lengths=("list", (1 << 20,)))
+    inp = make_inputs(w, seed=41)
+    print(f"B=1 L={1 << 20}", flush=True)
+    got = gpu_decode(inp, 0)
+    assert_parity(got, oracle.decode_inputs(inp), label="B=1 L=2^20")
+
+
+def test_a_thousand_short_sequences():
+    """B=1000 ragged sequences of 0..100 tokens (32 sequence groups in the combine; splits of
+    one or two tiles that span several sequences), paged and contiguous."""
+    rng = np.random.default_rng(42)
+    Ls = tuple(int(x) for x in rng.integers(0, 101, size=1000))
+    for w in (CONFIGS[2].replace(B=1000, lengths=("list", Ls)), CONFIGS[5].replace(B=1000, lengths=("list", Ls))):
+        inp = make_inputs(w, seed=42, poison=True)
+        got = gpu_decode(inp, 0)
+        assert np.all(got[[b for b, L in enumerate(Ls) if L == 0]] == 0)
+        assert_parity(got, oracle.decode_inputs(inp), label=f"B=1000 page={w.page_size}")
 
 
 def test_graph_replay_matches_eager():
