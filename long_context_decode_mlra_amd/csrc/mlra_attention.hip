@@ -415,7 +415,6 @@ void decode_kernel(DecodeArgs a) {
     te = __builtin_amdgcn_readfirstlane(te);
     const int L = scalar_read(a.seqlens + b);
     QOps<T, NB> q;
-    load_q<T, NB, HB>(a, b, head, head_ok, wq, sub, hh, q);
     floatx16 O[4] = {};
     float m_run = -INFINITY;
     float l_run = 0.f;
@@ -432,6 +431,8 @@ void decode_kernel(DecodeArgs a) {
     } else {
       issue_tile_loads<T, NB, HB>(a, b, L, ta, wave, lane, stg);
     }
+    // The queries load while the first tile is on its way.
+    load_q<T, NB, HB>(a, b, head, head_ok, wq, sub, hh, q);
     for (int k = ta; k < te; ++k) {
       const int slot = (k - ta) % G::kStages;
       unsigned char* buf = smem + slot * G::kTileBytes;
@@ -586,6 +587,8 @@ void decode_hs_kernel(DecodeArgs a) {
     te = __builtin_amdgcn_readfirstlane(te);
     const int L = scalar_read(a.seqlens + b);
 
+    // The first tile is on its way while the queries load.
+    issue_tile_dma<__bf16, NB, HB>(a, b, L, ta, wave, lane, smem);
     // Query operands: K step st < 8 covers latent channels qk_c0 + 32*st + 8*g .. +8; the RoPE
     // steps cover RoPE channels 32*rs + 8*g (NB = 2: rs = 0, 1; NB = 1: rs = cp).
     bf16x8 qv[kSteps];
@@ -603,7 +606,6 @@ void decode_hs_kernel(DecodeArgs a) {
     float m_run = -INFINITY;
     float l_run = 0.f;
 
-    issue_tile_dma<__bf16, NB, HB>(a, b, L, ta, wave, lane, smem);
     for (int k = ta; k < te; ++k) {
       unsigned char* buf = smem + ((k - ta) & 1) * G::kTileBytes;
       unsigned char* idle = smem + (((k - ta) & 1) ^ 1) * G::kTileBytes;
