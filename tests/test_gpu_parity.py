@@ -70,6 +70,18 @@ def test_small_ragged(name, num_splits):
     assert_parity(got, ref, label=f"{name}/splits={num_splits}", **tol)
 
 
+@pytest.mark.parametrize("name", ["mla_bf16", "mlra2_bf16", "mlra4_f32", "mla_f32"])
+@pytest.mark.parametrize("page_size", [32, 64])
+def test_paged_every_form(name, page_size):
+    """Paged caches (random page permutation, NaN in unowned rows) for the forms beyond MLRA-4
+    bf16: the split-head kernel (MLA joint rows, MLRA-2) and the fp32 kernels."""
+    w = SMALL[name].replace(B=4, lengths=("list", (1, 70, 333, 64)), page_size=page_size)
+    inp = make_inputs(w, seed=9, poison=True)
+    tol = dict(rel_l2=1e-4, max_abs=1e-3) if w.dtype == "f32" else {}
+    for splits in (0, 7):
+        assert_parity(gpu_decode(inp, splits), oracle.decode_inputs(inp), label=f"{name}/page={page_size}/splits={splits}", **tol)
+
+
 EDGE_LENGTHS = (0, 1, 2, 31, 32, 33, 63, 64, 65, 95, 96, 97, 0, 128, 129, 5)
 
 
