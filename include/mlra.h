@@ -122,7 +122,7 @@ int mlra_decode_workspace_size(const mlra_decode_params* p, size_t* bytes);
  *   block_table   int32 [B][max_pages_per_seq] or NULL
  *   seqlens       int32 [B] tokens cached per sequence, the new token included
  *   W_UV          fp32 [NB][h][d_latent][d_v], contiguous (row = latent channel)
- *   out           fp32 [B][h][d_v], contiguous; fully written
+ *   out           fp32 [B][h][d_v], contiguous, 16-byte aligned; fully written
  *   workspace     device scratch of at least mlra_decode_workspace_size bytes, 256-byte aligned;
  *                 no contents need to survive between calls
  * Base pointers of q_nope, q_rope, latent_cache, rope_cache and every row stride

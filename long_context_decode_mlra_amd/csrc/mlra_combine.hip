@@ -229,6 +229,8 @@ extern "C" int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, fl
   if (rc) return rc;
   if (p->batch == 0) return MLRA_OK;
   if (!W_UV || !out) return set_error(MLRA_ERR_NULL, "W_UV and out must be non-NULL");
+  if (!aligned16(out) || (reinterpret_cast<uintptr_t>(W_UV) & 3) != 0)
+    return set_error(MLRA_ERR_ALIGN, "out must be 16-byte and W_UV 4-byte aligned");
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   CombineArgs c;
   c.part_o = reinterpret_cast<const float*>(ws + lay.part_o_off);
@@ -260,6 +262,8 @@ extern "C" int mlra_decode(const void* q_nope, const void* q_rope, const void* l
                            const int32_t* block_table, const int32_t* seqlens, const float* W_UV, float* out,
                            const mlra_decode_params* p, void* workspace, size_t workspace_bytes, void* stream) {
   if (p && p->batch > 0 && (!W_UV || !out)) return set_error(MLRA_ERR_NULL, "W_UV and out must be non-NULL");
+  if (p && p->batch > 0 && (!aligned16(out) || (reinterpret_cast<uintptr_t>(W_UV) & 3) != 0))
+    return set_error(MLRA_ERR_ALIGN, "out must be 16-byte and W_UV 4-byte aligned");
   int rc = mlra_decode_splitkv(q_nope, q_rope, latent_cache, rope_cache, block_table, seqlens, p, workspace,
                                workspace_bytes, stream);
   if (rc) return rc;

@@ -126,6 +126,10 @@ def test_decode_argument_errors_before_any_launch():
     r = lib.mlra_decode(fake, fake, fake, fake, None, fake, fake, fake, ctypes.byref(p),
                         ctypes.c_void_p((1 << 20) + 16), n.value, None)
     assert r == -4
+    # misaligned output
+    r = lib.mlra_decode(fake, fake, fake, fake, None, fake, fake, ctypes.c_void_p((1 << 20) + 4), ctypes.byref(p),
+                        fake, n.value, None)
+    assert r == -4
     assert lib.mlra_decode_plan(fake, 4, 0, 4, fake, None) == -2
     assert lib.mlra_copy_bandwidth_probe(fake, ctypes.c_void_p((1 << 20) + 4), 64, None) == -4
 
