@@ -61,13 +61,16 @@ __device__ __forceinline__ void merge_in(MergeState& st, float m, float l, const
   for (int u = 0; u < 4; ++u) st.acc[u] += w * o[u];
 }
 
+// Workgroup barrier that orders LDS only (the W_UV loads issued first stay in flight).
+__device__ __forceinline__ void comb_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int NB>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int DL = kLatentTotal / NB;
   constexpr int kBatch = 4;  // slots loaded together
   constexpr int kSteps = kCombBlock / 2;  // K steps of the 32x32x2 MFMA
   __shared__ float ob[kCombBlock][kCombSeqs];  // merged block, k-major: ob[k][b]
-  __shared__ float st_red[18 * 256];            // per (slot part, pair): M, den, acc[16] (parts > 1)
+  __shared__ float st_red[18 * 128];            // per (receiving slot part, pair): M, den, acc[16]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -133,26 +136,30 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     }
   }
   if (S > 1) {
-    // Part r, field f (M, den, 16 accumulators), pair rem at st_red[(r * 18 + f) * NPP + rem].
-    if (live) {
-      st_red[(r * 18 + 0) * NPP + rem] = st.M;
-      st_red[(r * 18 + 1) * NPP + rem] = st.den;
+    // Tree over the slot parts in a fixed order: at each level, part r + half hands its state
+    // (M, den, 16 accumulators; each an unnormalised partial of the same form as a split's)
+    // to part r < half through st_red[(r * 18 + f) * NPP + rem]. The barriers wait on LDS only,
+    // so the W_UV loads stay in flight.
+    for (int half = S >> 1; half >= 1; half >>= 1) {
+      if (live && r >= half && r < 2 * half) {
+        float* sw = st_red + (r - half) * 18 * NPP + rem;
+        sw[0] = st.M;
+        sw[NPP] = st.den;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) st_red[(r * 18 + 2 + 4 * u + e) * NPP + rem] = st.acc[u][e];
-    }
-    __syncthreads();
-    if (live && r == 0) {
-      for (int rr = 1; rr < S; ++rr) {  // fixed order: part 0, 1, 2, ...
-        const float* sr = st_red + rr * 18 * NPP + rem;
+          for (int e = 0; e < 4; ++e) sw[(2 + 4 * u + e) * NPP] = st.acc[u][e];
+      }
+      comb_lds_barrier();
+      if (live && r < half) {
+        const float* sr = st_red + r * 18 * NPP + rem;
         floatx4 o1[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
           o1[u] = floatx4{sr[(2 + 4 * u) * NPP], sr[(3 + 4 * u) * NPP], sr[(4 + 4 * u) * NPP], sr[(5 + 4 * u) * NPP]};
-        // Each part is an unnormalised partial of the same form as a split's.
         merge_in(st, sr[0], sr[NPP], o1);
       }
+      comb_lds_barrier();
     }
   }
   if (r == 0) {
