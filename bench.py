@@ -34,7 +34,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed steps first (a fresh GPU needs a few dozen launches to reach steady clocks)")
-    ap.add_argument("--config", type=int, default=2, help="workload number (1-5); 2 is the headline")
+    ap.add_argument("--config", type=int, default=2, help="workload number (1-6); 2 is the headline")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = one split per resident workgroup slot")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")

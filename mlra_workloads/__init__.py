@@ -77,7 +77,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads of the decode benchmark. Seed = workload number.
+# The workloads of the decode benchmark. Seed = workload number.
 CONFIGS = {
     1: Workload("mlra4_f32_b1_h16_L1k", "f32", B=1, h=16, NB=4, DL=128, lengths=("fixed", 1024)),
     2: Workload("mlra4_bf16_b32_h32_L32k", "bf16", B=32, h=32, NB=4, DL=128, lengths=("fixed", 32768),
@@ -88,6 +88,8 @@ CONFIGS = {
                 joint=True),
     5: Workload("mlra4_paged_bf16_b64_h32_L1k-64k", "bf16", B=64, h=32, NB=4, DL=128,
                 lengths=("loguniform", 1024, 65536), page_size=64),
+    # MLRA-2 (two latent heads of 256 channels, rescale 1/sqrt(2)) at the headline shape.
+    6: Workload("mlra2_bf16_b32_h32_L32k", "bf16", B=32, h=32, NB=2, DL=256, lengths=("fixed", 32768)),
 }
 
 

@@ -195,7 +195,7 @@ def test_copy_and_read_probes():
 
 
 # ----------------------------------------------------------------- full-size workloads, sampled sequences
-FULL = {2: (0, 17, 31), 3: (0, 1, 2, 3), 4: (0, 31), 5: (0, 13, 40, 63)}
+FULL = {2: (0, 17, 31), 3: (0, 1, 2, 3), 4: (0, 31), 5: (0, 13, 40, 63), 6: (0, 31)}
 
 
 @pytest.mark.parametrize("cfg", sorted(FULL))
