@@ -16,6 +16,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -31,9 +32,10 @@ FLOP_PER_HEAD_TOKEN = 2 * (512 + 64) + 2 * 512     # QK (RoPE dot once) + PV, bo
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=50,
-                    help="untimed steps first (a fresh GPU needs a few dozen launches to reach steady clocks)")
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=2000,
+                    help="untimed steps first: on MI355X the whole-step time settles only after about 40 ms "
+                         "of back-to-back work (about 200 steps at the headline shape), 25 %% above steady before")
     ap.add_argument("--config", type=int, default=2, help="workload number (1-6); 2 is the headline")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = one split per resident workgroup slot")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -53,6 +55,15 @@ def parse():
     return ap.parse_args()
 
 
+def attention_kernel_name(w):
+    """The split-KV attention kernel the library launches for this workload."""
+    if w.dtype == "bf16" and w.NB == 4 and w.h <= 32:
+        return "decode_branch_kernel"
+    if w.dtype == "bf16" and w.NB < 4:
+        return "decode_hs_kernel"
+    return "decode_kernel"
+
+
 def algorithmic_bytes(inp):
     """Bytes the method must move once per step: cache rows of every cached token,
     queries, W_UV, the output, plus the int32 metadata."""
@@ -63,7 +74,7 @@ def algorithmic_bytes(inp):
     meta = B * 4 + (inp.block_table.numel() * 4 if inp.block_table is not None else 0)
     wuv = w.NB * h * w.DL * w.DV * 4
     out = B * h * w.DV * 4
-    return dict(decode_kernel=cache + q + meta, step=cache + q + meta + wuv + out, cache=cache)
+    return dict(attention=cache + q + meta, step=cache + q + meta + wuv + out, cache=cache)
 
 
 # The files the attention kernel is compiled from: a counter record taken on other sources is void.
@@ -109,14 +120,14 @@ def record_traffic(fetch_csv, write_csv, args):
     w_scale = copy_bytes / (pick(wr, "copy_kernel") * 1024)
     w = CONFIGS[args.config]
     inp = make_inputs(w, seed=args.config)
-    attn = lambda d: next(v for k, v in d.items() if "decode_kernel" in k or "decode_hs_kernel" in k)
+    attn = lambda d: next(v for k, v in d.items() if re.search(r"decode_(branch_|hs_)?kernel", k))
     fetch = attn(f) * 1024 * f_scale
     write = attn(wr) * 1024 * w_scale
     ab = algorithmic_bytes(inp)
     rec = {"workload": w.name, "kernel": "split-KV attention kernel", "fetch_bytes_per_launch": round(fetch),
            "write_bytes_per_launch": round(write), "hbm_bytes_per_launch": round(fetch + write),
-           "algorithmic_bytes_per_launch": ab["decode_kernel"],
-           "traffic_over_algorithmic": round((fetch + write) / ab["decode_kernel"], 4),
+           "algorithmic_bytes_per_launch": ab["attention"],
+           "traffic_over_algorithmic": round((fetch + write) / ab["attention"], 4),
            "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
            "calibration": f"copy_kernel of {copy_bytes} bytes read and written in the same runs",
            "kernel_sources": list(KERNEL_SOURCES), "kernel_source_sha256": kernel_source_hash()}
@@ -330,14 +341,13 @@ def main():
     tokens = inp.total_tokens
     flops = FLOP_PER_HEAD_TOKEN * w.h * tokens + 2 * len(inp.seqlens) * w.h * 512 * w.DV
     us = ms_per_step * 1e3
-    achieved = ab["decode_kernel"] / (dk_mean * 1e-3) / 1e9
+    achieved = ab["attention"] / (dk_mean * 1e-3) / 1e9
     trec = traffic_record(w.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": (trec["hbm_bytes_per_launch"] if trec else None),
-                "kernel": ("decode_hs_kernel" if (w.dtype == "bf16" and w.NB < 4) else "decode_kernel")
-                          + " (split-KV attention)",
-                "algorithmic_bytes_per_launch": ab["decode_kernel"],
+                "kernel": attention_kernel_name(w) + " (split-KV attention)",
+                "algorithmic_bytes_per_launch": ab["attention"],
                 "avg_launch_us": round(dk_mean * 1e3, 2)}
     result = {
         "metric": METRIC, "value": round(us, 2), "unit": "µs/step", "n_gpus": 1, "steps": args.steps,

@@ -27,6 +27,11 @@ ARCH = "gfx950"
 # Packed-fp32 VALU forms are kept out of every kernel.
 HIP_FLAGS = ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source extras. The one-wave-per-branch attention kernel runs one wave per SIMD; without
+# the MFMA VGPR form the compiler keeps its accumulators in AGPRs and copies them to and from
+# VGPRs every tile. The bf16 kernels that fit in 256 VGPRs compile to the same code either
+# way; the fp32 kernels that need more keep fewer values in AGPRs.
+SOURCE_FLAGS = {"mlra_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -53,8 +58,8 @@ def build(verbose: bool = False) -> str:
           os.path.join(CSRC, "mlra_params.cpp"), "-o", params_o])
     objs = [os.path.join(BUILD_DIR, os.path.splitext(s)[0] + ".o") for s in HIP_SOURCES]
     with ThreadPoolExecutor(max_workers=len(HIP_SOURCES)) as ex:
-        outs = list(ex.map(lambda so: _run([hipcc, *HIP_FLAGS, "-Wall", "-I", INCLUDE, "-c",
-                                            os.path.join(CSRC, so[0]), "-o", so[1]]),
+        outs = list(ex.map(lambda so: _run([hipcc, *HIP_FLAGS, *SOURCE_FLAGS.get(so[0], []), "-Wall", "-I",
+                                            INCLUDE, "-c", os.path.join(CSRC, so[0]), "-o", so[1]]),
                            zip(HIP_SOURCES, objs)))
     if verbose:
         for o in outs:

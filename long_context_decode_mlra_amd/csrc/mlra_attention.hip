@@ -10,14 +10,18 @@
 // (per-branch logit space 128 + 64, "Key Contributions" #2).
 //
 // Kernels (the split partials they write are merged by mlra_combine.hip)
-//   decode_kernel     one workgroup per split; streams 32-token tiles of the cache
-//                     (latent rows + RoPE rows) HBM -> LDS, computes S^T = K Q^T and
-//                     O^T += V^T P^T on bf16 (or fp32) MFMA for all query heads of the
-//                     split's sequence, keeps an fp32 online softmax per (latent head,
-//                     query head), and writes one partial (unnormalised O, running max,
-//                     running sum) per sequence it touches. MLRA-4 bf16, every fp32 form.
-//   decode_hs_kernel  the same for bf16 with one or two latent heads (MLA, MLRA-2), with
-//                     the query heads split across wave pairs.
+//   decode_branch_kernel  MLRA-4 bf16 with up to 32 query heads: one workgroup per split,
+//                     one wave per latent head (branch). Each wave streams its branch's
+//                     slice of 32-token tiles (latent channels + RoPE rows) HBM -> LDS
+//                     into a private ring, computes S^T = K Q^T and O^T += V^T P^T on bf16
+//                     MFMA for all query heads, keeps an fp32 online softmax per query
+//                     head, and writes one partial (unnormalised O, running max, running
+//                     sum) per sequence it touches. No workgroup barrier.
+//   decode_kernel     the same computation with whole tiles shared by the workgroup's waves
+//                     (workgroup barriers per tile): MLRA-4 bf16 with more than 32 query
+//                     heads, and every fp32 form.
+//   decode_hs_kernel  bf16 with one or two latent heads (MLA, MLRA-2), with the query
+//                     heads split across wave pairs.
 // Splitting is balanced over the flattened tiles of all sequences (the plan in mlra_device.h).
 #include <hip/hip_runtime.h>
 
@@ -34,10 +38,6 @@ namespace {
 // step, so allocating it in L2 / the Infinity Cache only evicts useful lines; streaming
 // loads measured about 7 TB/s against about 6.1 TB/s for default-policy loads on MI355X.
 constexpr int kStreamPolicy = 2;
-
-#ifndef MLRA_DMA_STAGES
-#define MLRA_DMA_STAGES 2
-#endif
 
 
 // Wait until at most N of this wave's vector-memory operations are outstanding.
@@ -140,9 +140,7 @@ struct Geo {
   // Loads go straight into LDS unless the idle tile buffer is needed for the
   // logit exchange between the waves that share one latent head.
   static constexpr bool kDirect = (kWPB == 1);
-  // Tile buffers: with direct loads, one bf16 head block may run a deeper ring (kStages
-  // tiles in flight while a wave waits for the oldest).
-  static constexpr int kStages = (kDirect && kEsz == 2 && HB == 1) ? MLRA_DMA_STAGES : 2;
+  static constexpr int kStages = 2;  // tile buffers
   static constexpr int kLds = kStages * kTileBytes;
   static_assert(kLatTile % 1024 == 0 && kTileBytes % 1024 == 0, "tile must be whole 1 KiB loads");
   static_assert(kWaves * 4096 <= kTileBytes, "logit exchange must fit the idle tile buffer");
@@ -384,7 +382,7 @@ __device__ __forceinline__ void tile_pv(const unsigned char* buf, int wq, int n,
 
 template <typename T, int NB, int HB>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, 256 * HB),
-                          amdgpu_waves_per_eu((sizeof(T) == 2 && Geo<T, NB, HB>::kStages == 2) ? 2 : 1, 2)))
+                          amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, 2)))
 void decode_kernel(DecodeArgs a) {
   using G = Geo<T, NB, HB>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[G::kLds];
@@ -533,6 +531,261 @@ void decode_kernel(DecodeArgs a) {
     }
     // The partial stores share the vector-memory counter with the next segment's tile loads.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+// ------------------------------------------------------------------ one wave per branch (MLRA-4, bf16, h <= 32)
+//
+// Four waves per workgroup; wave j owns latent head (branch) j outright. It streams its own
+// slice of every tile, the 128 channels of latent head j in the 32 latent rows (8 KiB) plus
+// the 32 RoPE rows (4 KiB), into a private LDS ring of kBranchStages tiles, and computes its
+// branch's logits (latent and RoPE channels), softmax and PV alone. No wave waits for another:
+// there is no workgroup barrier, and while a wave computes one tile the next kBranchStages-1
+// of its own are in flight. All four waves load the same RoPE rows, non-temporally like the
+// latent slices; most of the repeats are still served by L2 (measured: 4 % more HBM reads
+// than one copy). An L2-allocating policy for the RoPE rows removes that 4 % on clean caches
+// but made the kernel up to 1.5x slower on MI355X when the work before it left the caches
+// full of dirty lines (a write of 128 MiB or more). The ring takes 144 KiB, so one workgroup
+// runs per compute unit, and the split count (one split per resident workgroup) is half that
+// of decode_kernel, which halves the partials. MFMA layout as in decode_kernel: S^T = K Q^T
+// and O^T += V^T P^T on bf16 32x32x16, tokens as M and the 32 query heads as N.
+constexpr int kBranchStages = 3;
+constexpr int kBrLatRow = 128 * 2;                 // bytes: one latent head of one token
+constexpr int kBrRopeRow = kDRope * 2;             // bytes: one RoPE row
+constexpr int kBrLat = kTile * kBrLatRow;          // 8 KiB
+constexpr int kBrTile = kBrLat + kTile * kBrRopeRow;  // 12 KiB per wave and tile
+constexpr int kBrLoads = kBrTile / 1024;           // 12 loads of 64 lanes x 16 bytes
+static_assert(kBrLat == 8 * 1024 && kBrLoads == 12, "branch tile geometry");
+static_assert((kBranchStages - 1) * kBrLoads < 64, "vmcnt immediate");
+static_assert(4 * kBranchStages * kBrTile <= 160 * 1024, "LDS");
+
+// s_waitcnt immediates for __builtin_amdgcn_s_waitcnt (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4, lgkmcnt 11:8). Unlike inline asm, the builtin is seen by the compiler's
+// own wait insertion, which then knows the waited-for loads are complete.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitVm0Lgkm0 = (7 << 4);
+
+// Latent slice rows: chunk c (of 16) of token t sits at chunk position c ^ (t & 15).
+__device__ __forceinline__ int br_lat_swizzle(int t) { return t & 15; }
+
+// Wave j's 12 loads of one tile: 8 latent loads (rows 4i .. 4i+3; lane l -> row 4i + l/16,
+// chunk position l%16), then 4 RoPE loads (rows 8i .. 8i+7; lane l -> row 8i + l/8, chunk
+// position l%8). Rows past the sequence end re-read its last row (their logits are masked).
+__device__ __forceinline__ void br_issue_tile(const DecodeArgs& a, int b, int L, int tile, int j, int lane,
+                                              unsigned char* buf) {
+  const TileRows tr = tile_rows(a, b, L, tile);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const unsigned char* src =
+        tr.lat + (min(r, tr.last) * int(a.lat_stride) + j * kBrLatRow + (((lane & 15) ^ br_lat_swizzle(r)) << 4));
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, 0,
+                                     kStreamPolicy);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 8 * i + (lane >> 3);
+    const unsigned char* src =
+        tr.rope + (min(r, tr.last) * int(a.rope_stride) + (((lane & 7) ^ rope_swizzle<kBrRopeRow>(r)) << 4));
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)(buf + kBrLat + i * 1024), 16, 0,
+                                     kStreamPolicy);
+  }
+}
+
+// Wait until this wave's loads of the oldest tile in flight have landed, with `later`
+// (0 <= later < S, wave-uniform) tiles issued after it still in flight.
+template <int S>
+__device__ __forceinline__ void br_wait_tile(int later) {
+  if constexpr (S > 1) {
+    if (later == S - 1) {
+      wait_vmcnt<(S - 1) * kBrLoads>();
+      return;
+    }
+    br_wait_tile<S - 1>(later);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
+// Launch bounds allow one wave per SIMD (the LDS ring admits no more). Built with the MFMA
+// VGPR form (-amdgpu-mfma-vgpr-form): otherwise the compiler keeps the accumulators in AGPRs
+// and copies them to and from VGPRs every tile.
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void decode_branch_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kBranchStages * kBrTile];
+  const int lane = threadIdx.x & 63;
+  const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // latent head of this wave
+  const int n = lane & 31;  // query head (MFMA column) and token row of the A operand
+  const int hh = lane >> 5;
+  const bool head_ok = n < a.h;
+  unsigned char* ring = smem + j * (kBranchStages * kBrTile);
+
+  const Plan plan = split_plan(a);
+  const int g = blockIdx.x;
+  if (g == 0 && j == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
+  if (g >= plan.G) return;
+  SegmentWalk walk = begin_walk(a.seqlens, a.B, g, plan);
+
+  int b, ta, te;
+  while (next_segment(a.seqlens, a.B, walk, b, ta, te)) {
+    b = __builtin_amdgcn_readfirstlane(b);
+    ta = __builtin_amdgcn_readfirstlane(ta);
+    te = __builtin_amdgcn_readfirstlane(te);
+    const int L = scalar_read(a.seqlens + b);
+    // Query operands: latent K step ks covers channels 16*ks + 8*hh .. +8 of latent head j,
+    // RoPE K step rs channels 16*rs + 8*hh .. +8. Lanes past h load head 0 and are zeroed.
+    bf16x8 ql[8], qr[4];
+    {
+      const unsigned char* qn = a.q_nope + int64_t(b) * a.q_sb + int64_t(head_ok ? n : 0) * a.q_sh + 256 * j;
+      const unsigned char* qp = a.q_rope + int64_t(b) * a.qr_sb + int64_t(head_ok ? n : 0) * a.qr_sh;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) ql[ks] = *reinterpret_cast<const bf16x8*>(qn + (16 * ks + 8 * hh) * 2);
+#pragma unroll
+      for (int rs = 0; rs < 4; ++rs) qr[rs] = *reinterpret_cast<const bf16x8*>(qp + (16 * rs + 8 * hh) * 2);
+    }
+    floatx16 O[4] = {};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    // The first kBranchStages-1 tiles go out while the queries are in flight; then wait for
+    // the queries only. The wait is a builtin so that the compiler, too, knows the query
+    // registers complete: it places no wait of its own on them inside the tile loop.
+    int issued = 0;
+#pragma unroll
+    for (int st = 0; st < kBranchStages - 1; ++st)
+      if (ta + st < te) {
+        br_issue_tile(a, b, L, ta + st, j, lane, ring + st * kBrTile);
+        ++issued;
+      }
+    if (issued == kBranchStages - 1)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((kBranchStages - 1) * kBrLoads));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if (!head_ok) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) ql[ks] = bf16x8{};
+#pragma unroll
+      for (int rs = 0; rs < 4; ++rs) qr[rs] = bf16x8{};
+    }
+
+    for (int k = ta; k < te; ++k) {
+      const unsigned char* buf = ring + ((k - ta) % kBranchStages) * kBrTile;
+      if (k + kBranchStages - 1 < te) {
+        // Tile k+S-1 reuses tile k-1's buffer: this wave's reads of it have returned.
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        br_issue_tile(a, b, L, k + kBranchStages - 1, j, lane,
+                      ring + ((k - ta + kBranchStages - 1) % kBranchStages) * kBrTile);
+      }
+      br_wait_tile<kBranchStages>(min(kBranchStages - 1, te - 1 - k));
+
+      // S^T[token][head]: row n of the A operand is token n; chunk 2*ks + hh of latent row n
+      // sits at (2*ks + hh) ^ br_lat_swizzle(n), of RoPE row n at (2*rs + hh) ^ rope_swizzle(n).
+      floatx16 s = {};
+      {
+        const unsigned char* lrow = buf + n * kBrLatRow;
+        const unsigned char* rrow = buf + kBrLat + n * kBrRopeRow;
+        const int sw = br_lat_swizzle(n);
+        const int rsw = rope_swizzle<kBrRopeRow>(n);
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 kk = *reinterpret_cast<const bf16x8*>(lrow + (((2 * ks + hh) ^ sw) << 4));
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, ql[ks], s, 0, 0, 0);
+        }
+#pragma unroll
+        for (int rs = 0; rs < 4; ++rs) {
+          const bf16x8 kk = *reinterpret_cast<const bf16x8*>(rrow + (((2 * rs + hh) ^ rsw) << 4));
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qr[rs], s, 0, 0, 0);
+        }
+      }
+      const int n_valid = L - k * kTile;
+      if (n_valid < kTile) {
+        // Register r of lane half hh holds token 8*(r>>2) + 4*hh + (r&3).
+        const int lim = n_valid - 4 * hh;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (8 * (r >> 2) + (r & 3) >= lim) s[r] = -INFINITY;
+      }
+      // Online softmax in log2 units: x = s * sm_scale * log2(e).
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mt = mx * a.c;
+      const bool raise = mt > m_run + kRescaleSlack;
+      if (__ballot(raise)) {
+        const float mnew = raise ? mt : m_run;
+        const float alpha = (mnew == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
+        l_run *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) O[mb] *= alpha;
+        m_run = mnew;
+      }
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -m_run));
+        psum += s[r];
+      }
+      l_run += psum;
+
+      // O^T[channel][head] += V^T P^T: K step ks covers tokens 16*ks .. +16; lane (n, hh)
+      // takes token 16*ks + 8*(e>>2) + 4*hh + (e&3) as K index 8*hh + e. Output row m of
+      // M-block mb is channel 4*m + mb: each lane reads channels 4n .. 4n+3 (8 bytes).
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 v = __builtin_convertvector((floatx2{s[8 * ks + e], s[8 * ks + e + 1]}), bf16x2);
+          pb[e] = v[0];
+          pb[e + 1] = v[1];
+        }
+        u32x2 d[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tau = 16 * ks + 8 * (e >> 2) + 4 * hh + (e & 3);
+          d[e] = *reinterpret_cast<const u32x2*>(buf + tau * kBrLatRow + (((n >> 1) ^ br_lat_swizzle(tau)) << 4) +
+                                                 ((n & 1) << 3));
+        }
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const uint32_t sel = (mb & 1) ? 0x07060302u : 0x05040100u;
+          u32x4 av;
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const uint32_t lo = (mb < 2) ? d[2 * pp][0] : d[2 * pp][1];
+            const uint32_t hi = (mb < 2) ? d[2 * pp + 1][0] : d[2 * pp + 1][1];
+            av[pp] = __builtin_amdgcn_perm(hi, lo, sel);
+          }
+          O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb, O[mb], 0, 0, 0);
+        }
+      }
+    }
+
+    // Partial of split g for sequence b, slot g + b: channel 32*gg + 16*hh + 4*i + mb of
+    // latent head j is O[mb][4*gg + i].
+    const int64_t pslot = int64_t(g) + b;
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (head_ok) {
+      float* dst = a.part_o + ((pslot * 4 + j) * a.h + n) * 128;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<floatx4*>(dst + 32 * gg + 16 * hh + 4 * i) =
+              floatx4{O[0][4 * gg + i], O[1][4 * gg + i], O[2][4 * gg + i], O[3][4 * gg + i]};
+      if (hh == 0) {
+        float* ml = a.part_ml + ((pslot * 4 + j) * a.h + n) * 2;
+        ml[0] = m_run;
+        ml[1] = l_tot;
+      }
+    }
+    // Stores drained and LDS reads returned before the next segment reuses the ring (a
+    // builtin: the compiler's own wait tracking then starts the next segment clean).
+    __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+    asm volatile("" ::: "memory");
   }
 }
 
@@ -755,7 +1008,7 @@ DecodeFn pick_decode(int dtype, int nb, int hb) {
 #define MLRA_PICK(T, NB_)                                                        \
   if (nb == NB_) return hb == 1 ? decode_kernel<T, NB_, 1> : decode_kernel<T, NB_, 2>;
   if (dtype == MLRA_BF16) {
-    MLRA_PICK(__bf16, 4)
+    if (nb == 4) return hb == 1 ? decode_branch_kernel : decode_kernel<__bf16, 4, 2>;
     if (nb == 2) return hb == 1 ? decode_hs_kernel<2, 1> : decode_hs_kernel<2, 2>;
     if (nb == 1) return hb == 1 ? decode_hs_kernel<1, 1> : decode_hs_kernel<1, 2>;
   } else {
