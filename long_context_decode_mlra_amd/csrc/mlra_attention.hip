@@ -565,32 +565,53 @@ static_assert(4 * kBranchStages * kBrTile <= 160 * 1024, "LDS");
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kWaitVm0Lgkm0 = (7 << 4);
 
+// x combined with the value of lane l ^ 32, in every lane, by one v_permlane32_swap: with both
+// operands x, result 0 holds the low half of x in both halves and result 1 the high half.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return fmaxf(__builtin_bit_cast(float, uint32_t(r[0])), __builtin_bit_cast(float, uint32_t(r[1])));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  return __builtin_bit_cast(float, uint32_t(r[0])) + __builtin_bit_cast(float, uint32_t(r[1]));
+}
+
 // Latent slice rows: chunk c (of 16) of token t sits at chunk position c ^ (t & 15).
 __device__ __forceinline__ int br_lat_swizzle(int t) { return t & 15; }
 
 // Wave j's 12 loads of one tile: 8 latent loads (rows 4i .. 4i+3; lane l -> row 4i + l/16,
 // chunk position l%16), then 4 RoPE loads (rows 8i .. 8i+7; lane l -> row 8i + l/8, chunk
 // position l%8). Rows past the sequence end re-read its last row (their logits are masked).
-__device__ __forceinline__ void br_issue_tile(const DecodeArgs& a, int b, int L, int tile, int j, int lane,
-                                              unsigned char* buf) {
-  const TileRows tr = tile_rows(a, b, L, tile);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
+// Byte offset of load i for this lane from the tile's first row, clamped to row `last`.
+__device__ __forceinline__ uint32_t br_load_offset(const DecodeArgs& a, int i, int j, int lane, int last) {
+  if (i < 8) {
     const int r = 4 * i + (lane >> 4);
-    const unsigned char* src =
-        tr.lat + (min(r, tr.last) * int(a.lat_stride) + j * kBrLatRow + (((lane & 15) ^ br_lat_swizzle(r)) << 4));
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, 0,
-                                     kStreamPolicy);
+    return uint32_t(min(r, last) * int(a.lat_stride) + j * kBrLatRow + (((lane & 15) ^ br_lat_swizzle(r)) << 4));
   }
+  const int r = 8 * (i - 8) + (lane >> 3);
+  return uint32_t(min(r, last) * int(a.rope_stride) + (((lane & 7) ^ rope_swizzle<kBrRopeRow>(r)) << 4));
+}
+
+// `full` holds this lane's offsets for a whole tile (computed once): a tile that does not end
+// a sequence is then addressed as scalar row base + 32-bit lane offset, with no vector
+// arithmetic. Offsets inside one tile fit 32 bits (32 rows, strides below 2^25 bytes).
+__device__ __forceinline__ void br_issue_tile(const DecodeArgs& a, int b, int L, int tile, int j, int lane,
+                                              unsigned char* buf, const uint32_t (&full)[kBrLoads]) {
+  const TileRows tr = tile_rows(a, b, L, tile);
+  if (tr.last == kTile - 1) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 8 * i + (lane >> 3);
-    const unsigned char* src =
-        tr.rope + (min(r, tr.last) * int(a.rope_stride) + (((lane & 7) ^ rope_swizzle<kBrRopeRow>(r)) << 4));
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)(buf + kBrLat + i * 1024), 16, 0,
-                                     kStreamPolicy);
+    for (int i = 0; i < kBrLoads; ++i)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((i < 8 ? tr.lat : tr.rope) + full[i]),
+                                       (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, 0, kStreamPolicy);
+  } else {
+#pragma unroll
+    for (int i = 0; i < kBrLoads; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)((i < 8 ? tr.lat : tr.rope) +
+                                                            br_load_offset(a, i, j, lane, tr.last)),
+          (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, 0, kStreamPolicy);
   }
 }
 
@@ -621,6 +642,9 @@ void decode_branch_kernel(DecodeArgs a) {
   const int hh = lane >> 5;
   const bool head_ok = n < a.h;
   unsigned char* ring = smem + j * (kBranchStages * kBrTile);
+  uint32_t full[kBrLoads];
+#pragma unroll
+  for (int i = 0; i < kBrLoads; ++i) full[i] = br_load_offset(a, i, j, lane, kTile - 1);
 
   const Plan plan = split_plan(a);
   const int g = blockIdx.x;
@@ -656,7 +680,7 @@ void decode_branch_kernel(DecodeArgs a) {
 #pragma unroll
     for (int st = 0; st < kBranchStages - 1; ++st)
       if (ta + st < te) {
-        br_issue_tile(a, b, L, ta + st, j, lane, ring + st * kBrTile);
+        br_issue_tile(a, b, L, ta + st, j, lane, ring + st * kBrTile, full);
         ++issued;
       }
     if (issued == kBranchStages - 1)
@@ -676,7 +700,7 @@ void decode_branch_kernel(DecodeArgs a) {
         // Tile k+S-1 reuses tile k-1's buffer: this wave's reads of it have returned.
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         br_issue_tile(a, b, L, k + kBranchStages - 1, j, lane,
-                      ring + ((k - ta + kBranchStages - 1) % kBranchStages) * kBrTile);
+                      ring + ((k - ta + kBranchStages - 1) % kBranchStages) * kBrTile, full);
       }
       br_wait_tile<kBranchStages>(min(kBranchStages - 1, te - 1 - k));
 
@@ -711,7 +735,7 @@ void decode_branch_kernel(DecodeArgs a) {
       float mx = s[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = halves_max(mx);
       const float mt = mx * a.c;
       const bool raise = mt > m_run + kRescaleSlack;
       if (__ballot(raise)) {
@@ -767,7 +791,7 @@ void decode_branch_kernel(DecodeArgs a) {
     // Partial of split g for sequence b, slot g + b: channel 32*gg + 16*hh + 4*i + mb of
     // latent head j is O[mb][4*gg + i].
     const int64_t pslot = int64_t(g) + b;
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = halves_sum(l_run);
     if (head_ok) {
       float* dst = a.part_o + ((pslot * 4 + j) * a.h + n) * 128;
 #pragma unroll
