@@ -358,7 +358,8 @@ extern "C" int mlra_gqa_decode(const void* q, const void* k_cache, const void* v
   int rc = gqa_prepare(p, seqlens, workspace, workspace_bytes, &G, &lay);
   if (rc) return rc;
   if (p->batch == 0) return MLRA_OK;
-  if (!q || !k_cache || !v_cache || !out) return set_error(MLRA_ERR_NULL, "q, k_cache, v_cache and out must be non-NULL");
+  if (!q || !k_cache || !v_cache || !out)
+    return set_error(MLRA_ERR_NULL, "q, k_cache, v_cache and out must be non-NULL");
   if ((p->page_size > 0) != (block_table != nullptr))
     return set_error(MLRA_ERR_NULL, "block_table must be given exactly when page_size > 0");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))

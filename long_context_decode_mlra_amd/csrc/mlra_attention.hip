@@ -584,6 +584,13 @@ __device__ __forceinline__ int br_lat_swizzle(int t) { return t & 15; }
 // Wave j's 12 loads of one tile: 8 latent loads (rows 4i .. 4i+3; lane l -> row 4i + l/16,
 // chunk position l%16), then 4 RoPE loads (rows 8i .. 8i+7; lane l -> row 8i + l/8, chunk
 // position l%8). Rows past the sequence end re-read its last row (their logits are masked).
+// One 16-byte non-temporal load per lane straight into LDS; the wave's 64 lanes fill
+// [dst, dst + 1024) in lane order.
+__device__ __forceinline__ void dma16(const unsigned char* src, unsigned char* dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0, kStreamPolicy);
+}
+
 // Byte offset of load i for this lane from the tile's first row, clamped to row `last`.
 __device__ __forceinline__ uint32_t br_load_offset(const DecodeArgs& a, int i, int j, int lane, int last) {
   if (i < 8) {
@@ -602,16 +609,11 @@ __device__ __forceinline__ void br_issue_tile(const DecodeArgs& a, int b, int L,
   const TileRows tr = tile_rows(a, b, L, tile);
   if (tr.last == kTile - 1) {
 #pragma unroll
-    for (int i = 0; i < kBrLoads; ++i)
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)((i < 8 ? tr.lat : tr.rope) + full[i]),
-                                       (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, 0, kStreamPolicy);
+    for (int i = 0; i < kBrLoads; ++i) dma16((i < 8 ? tr.lat : tr.rope) + full[i], buf + i * 1024);
   } else {
 #pragma unroll
     for (int i = 0; i < kBrLoads; ++i)
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)((i < 8 ? tr.lat : tr.rope) +
-                                                            br_load_offset(a, i, j, lane, tr.last)),
-          (__attribute__((address_space(3))) void*)(buf + i * 1024), 16, 0, kStreamPolicy);
+      dma16((i < 8 ? tr.lat : tr.rope) + br_load_offset(a, i, j, lane, tr.last), buf + i * 1024);
   }
 }
 
@@ -1067,8 +1069,8 @@ int resident_splits(const mlra_decode_params& p, int32_t* out, int* cus_out = nu
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
   int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(pick_decode(p.dtype, p.num_branches, hb)),
-                                                   256 * hb, 0);
+  const void* kernel = reinterpret_cast<const void*>(pick_decode(p.dtype, p.num_branches, hb));
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256 * hb, 0);
   if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
   if (per_cu < 1) per_cu = 1;
   const int n = cus * per_cu;
