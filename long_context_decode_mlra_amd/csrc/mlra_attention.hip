@@ -252,9 +252,17 @@ __device__ __forceinline__ void issue_tile_loads(const DecodeArgs& a, int b, int
   }
 }
 
+// One 16-byte non-temporal load per lane straight into LDS; the wave's 64 lanes fill
+// [dst, dst + 1024) in lane order.
+__device__ __forceinline__ void dma16(const unsigned char* src, unsigned char* dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0, kStreamPolicy);
+}
+
 // Direct loader: this wave's loads of one tile go straight from HBM into LDS
 // (each load writes 64 lanes x 16 bytes contiguously at the given LDS address).
-// Completion is tracked by the wave's vector-memory counter.
+// Completion is tracked by the wave's vector-memory counter. (Whole-tile offsets computed
+// once, as decode_branch_kernel does, measured 2 us slower in decode_hs_kernel.)
 template <typename T, int NB, int HB>
 __device__ __forceinline__ void issue_tile_dma(const DecodeArgs& a, int b, int L, int tile, int wave, int lane,
                                                unsigned char* buf) {
@@ -263,12 +271,7 @@ __device__ __forceinline__ void issue_tile_dma(const DecodeArgs& a, int b, int L
 #pragma unroll
   for (int i = 0; i < G::kInstPerWave; ++i) {
     const int inst = wave + i * G::kWaves;
-    if (inst < G::kInst) {
-      const unsigned char* src = load_src<T, NB, HB>(a, tr, inst, lane);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(buf + inst * 1024), 16, 0,
-                                       kStreamPolicy);
-    }
+    if (inst < G::kInst) dma16(load_src<T, NB, HB>(a, tr, inst, lane), buf + inst * 1024);
   }
 }
 
@@ -565,17 +568,22 @@ static_assert(4 * kBranchStages * kBrTile <= 160 * 1024, "LDS");
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kWaitVm0Lgkm0 = (7 << 4);
 
-// x combined with the value of lane l ^ 32, in every lane, by one v_permlane32_swap: with both
-// operands x, result 0 holds the low half of x in both halves and result 1 the high half.
-__device__ __forceinline__ float halves_max(float x) {
+// x combined with the value of lane l ^ 32, in every lane, by one v_permlane32_swap with both
+// operands x: result 0 then holds the low half of x in both halves and result 1 the high half,
+// so every lane combines the same two values in the same order. (In the kernels with two
+// workgroups per CU the LDS shuffle measured as fast or faster, so they keep it.)
+__device__ __forceinline__ floatx2 halves_pair(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
                                                   false, false);
-  return fmaxf(__builtin_bit_cast(float, uint32_t(r[0])), __builtin_bit_cast(float, uint32_t(r[1])));
+  return floatx2{__builtin_bit_cast(float, uint32_t(r[0])), __builtin_bit_cast(float, uint32_t(r[1]))};
+}
+__device__ __forceinline__ float halves_max(float x) {
+  const floatx2 p = halves_pair(x);
+  return fmaxf(p[0], p[1]);
 }
 __device__ __forceinline__ float halves_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
-                                                  false, false);
-  return __builtin_bit_cast(float, uint32_t(r[0])) + __builtin_bit_cast(float, uint32_t(r[1]));
+  const floatx2 p = halves_pair(x);
+  return p[0] + p[1];
 }
 
 // Latent slice rows: chunk c (of 16) of token t sits at chunk position c ^ (t & 15).
@@ -584,13 +592,6 @@ __device__ __forceinline__ int br_lat_swizzle(int t) { return t & 15; }
 // Wave j's 12 loads of one tile: 8 latent loads (rows 4i .. 4i+3; lane l -> row 4i + l/16,
 // chunk position l%16), then 4 RoPE loads (rows 8i .. 8i+7; lane l -> row 8i + l/8, chunk
 // position l%8). Rows past the sequence end re-read its last row (their logits are masked).
-// One 16-byte non-temporal load per lane straight into LDS; the wave's 64 lanes fill
-// [dst, dst + 1024) in lane order.
-__device__ __forceinline__ void dma16(const unsigned char* src, unsigned char* dst) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)dst, 16, 0, kStreamPolicy);
-}
-
 // Byte offset of load i for this lane from the tile's first row, clamped to row `last`.
 __device__ __forceinline__ uint32_t br_load_offset(const DecodeArgs& a, int i, int j, int lane, int last) {
   if (i < 8) {
