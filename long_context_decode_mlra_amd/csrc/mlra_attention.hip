@@ -16,7 +16,9 @@
 //                     into a private ring, computes S^T = K Q^T and O^T += V^T P^T on bf16
 //                     MFMA for all query heads, keeps an fp32 online softmax per query
 //                     head, and writes one partial (unnormalised O, running max, running
-//                     sum) per sequence it touches. No workgroup barrier.
+//                     sum) per sequence it touches; a split that spans sequences keeps its
+//                     first partial in registers and stores it after its loads are done.
+//                     No workgroup barrier.
 //   decode_kernel     the same computation with whole tiles shared by the workgroup's waves
 //                     (workgroup barriers per tile): MLRA-4 bf16 with more than 32 query
 //                     heads, and every fp32 form.
@@ -633,6 +635,171 @@ __device__ __forceinline__ void br_wait_tile(int later) {
   }
 }
 
+// Online-softmax state of one wave for one segment: unnormalised O (channel 32*gg + 16*hh +
+// 4*i + mb of the wave's latent head is O[mb][4*gg + i]), running max m in log2 units, and
+// the lane half's share l of the denominator.
+struct BrAcc {
+  floatx16 O[4];
+  float m, l;
+};
+
+// Tiles [ta, te) of sequence b for latent head j, from the queries to the softmax state.
+__device__ __forceinline__ void br_segment(const DecodeArgs& a, int b, int ta, int te, int j, int lane,
+                                           bool head_ok, unsigned char* ring, const uint32_t (&full)[kBrLoads],
+                                           BrAcc& acc) {
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int L = scalar_read(a.seqlens + b);
+  // Query operands: latent K step ks covers channels 16*ks + 8*hh .. +8 of latent head j,
+  // RoPE K step rs channels 16*rs + 8*hh .. +8. Lanes past h load head 0 and are zeroed.
+  bf16x8 ql[8], qr[4];
+  {
+    const unsigned char* qn = a.q_nope + int64_t(b) * a.q_sb + int64_t(head_ok ? n : 0) * a.q_sh + 256 * j;
+    const unsigned char* qp = a.q_rope + int64_t(b) * a.qr_sb + int64_t(head_ok ? n : 0) * a.qr_sh;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ql[ks] = *reinterpret_cast<const bf16x8*>(qn + (16 * ks + 8 * hh) * 2);
+#pragma unroll
+    for (int rs = 0; rs < 4; ++rs) qr[rs] = *reinterpret_cast<const bf16x8*>(qp + (16 * rs + 8 * hh) * 2);
+  }
+  floatx16 (&O)[4] = acc.O;
+  float& m_run = acc.m;
+  float& l_run = acc.l;
+  for (int mb = 0; mb < 4; ++mb) O[mb] = floatx16{};
+  m_run = -INFINITY;
+  l_run = 0.f;
+
+  // The first kBranchStages-1 tiles go out while the queries are in flight; then wait for
+  // the queries only. The wait is a builtin so that the compiler, too, knows the query
+  // registers complete: it places no wait of its own on them inside the tile loop.
+  int issued = 0;
+#pragma unroll
+  for (int st = 0; st < kBranchStages - 1; ++st)
+    if (ta + st < te) {
+      br_issue_tile(a, b, L, ta + st, j, lane, ring + st * kBrTile, full);
+      ++issued;
+    }
+  if (issued == kBranchStages - 1)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((kBranchStages - 1) * kBrLoads));
+  else
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  if (!head_ok) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ql[ks] = bf16x8{};
+#pragma unroll
+    for (int rs = 0; rs < 4; ++rs) qr[rs] = bf16x8{};
+  }
+
+  for (int k = ta; k < te; ++k) {
+    const unsigned char* buf = ring + ((k - ta) % kBranchStages) * kBrTile;
+    if (k + kBranchStages - 1 < te) {
+      // Tile k+S-1 reuses tile k-1's buffer: this wave's reads of it have returned.
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      br_issue_tile(a, b, L, k + kBranchStages - 1, j, lane,
+                    ring + ((k - ta + kBranchStages - 1) % kBranchStages) * kBrTile, full);
+    }
+    br_wait_tile<kBranchStages>(min(kBranchStages - 1, te - 1 - k));
+
+    // S^T[token][head]: row n of the A operand is token n; chunk 2*ks + hh of latent row n
+    // sits at (2*ks + hh) ^ br_lat_swizzle(n), of RoPE row n at (2*rs + hh) ^ rope_swizzle(n).
+    floatx16 s = {};
+    {
+      const unsigned char* lrow = buf + n * kBrLatRow;
+      const unsigned char* rrow = buf + kBrLat + n * kBrRopeRow;
+      const int sw = br_lat_swizzle(n);
+      const int rsw = rope_swizzle<kBrRopeRow>(n);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 kk = *reinterpret_cast<const bf16x8*>(lrow + (((2 * ks + hh) ^ sw) << 4));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, ql[ks], s, 0, 0, 0);
+      }
+#pragma unroll
+      for (int rs = 0; rs < 4; ++rs) {
+        const bf16x8 kk = *reinterpret_cast<const bf16x8*>(rrow + (((2 * rs + hh) ^ rsw) << 4));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qr[rs], s, 0, 0, 0);
+      }
+    }
+    const int n_valid = L - k * kTile;
+    if (n_valid < kTile) {
+      // Register r of lane half hh holds token 8*(r>>2) + 4*hh + (r&3).
+      const int lim = n_valid - 4 * hh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) >= lim) s[r] = -INFINITY;
+    }
+    // Online softmax in log2 units: x = s * sm_scale * log2(e).
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = halves_max(mx);
+    const float mt = mx * a.c;
+    const bool raise = mt > m_run + kRescaleSlack;
+    if (__ballot(raise)) {
+      const float mnew = raise ? mt : m_run;
+      const float alpha = (mnew == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) O[mb] *= alpha;
+      m_run = mnew;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -m_run));
+      psum += s[r];
+    }
+    l_run += psum;
+
+    // O^T[channel][head] += V^T P^T: K step ks covers tokens 16*ks .. +16; lane (n, hh)
+    // takes token 16*ks + 8*(e>>2) + 4*hh + (e&3) as K index 8*hh + e. Output row m of
+    // M-block mb is channel 4*m + mb: each lane reads channels 4n .. 4n+3 (8 bytes).
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 v = __builtin_convertvector((floatx2{s[8 * ks + e], s[8 * ks + e + 1]}), bf16x2);
+        pb[e] = v[0];
+        pb[e + 1] = v[1];
+      }
+      u32x2 d[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tau = 16 * ks + 8 * (e >> 2) + 4 * hh + (e & 3);
+        d[e] = *reinterpret_cast<const u32x2*>(buf + tau * kBrLatRow + (((n >> 1) ^ br_lat_swizzle(tau)) << 4) +
+                                               ((n & 1) << 3));
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const uint32_t sel = (mb & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 av;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const uint32_t lo = (mb < 2) ? d[2 * pp][0] : d[2 * pp][1];
+          const uint32_t hi = (mb < 2) ? d[2 * pp + 1][0] : d[2 * pp + 1][1];
+          av[pp] = __builtin_amdgcn_perm(hi, lo, sel);
+        }
+        O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb, O[mb], 0, 0, 0);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void br_store_partial(const DecodeArgs& a, int64_t pslot, int j, int n, int hh,
+                                                 const BrAcc& acc, float l_tot) {
+  float* dst = a.part_o + ((pslot * 4 + j) * a.h + n) * 128;
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<floatx4*>(dst + 32 * gg + 16 * hh + 4 * i) =
+          floatx4{acc.O[0][4 * gg + i], acc.O[1][4 * gg + i], acc.O[2][4 * gg + i], acc.O[3][4 * gg + i]};
+  if (hh == 0) {
+    float* ml = a.part_ml + ((pslot * 4 + j) * a.h + n) * 2;
+    ml[0] = acc.m;
+    ml[1] = l_tot;
+  }
+}
+
 // Launch bounds allow one wave per SIMD (the LDS ring admits no more). Built with the MFMA
 // VGPR form (-amdgpu-mfma-vgpr-form): otherwise the compiler keeps the accumulators in AGPRs
 // and copies them to and from VGPRs every tile.
@@ -655,165 +822,42 @@ void decode_branch_kernel(DecodeArgs a) {
   if (g >= plan.G) return;
   SegmentWalk walk = begin_walk(a.seqlens, a.B, g, plan);
 
+  // The split's partial for sequence b goes to slot g + b. A store issued while tiles stream
+  // in delays every later tile wait (the vector-memory counter retires loads and stores in
+  // order), so when a split spans sequences the first segment's partial stays in registers
+  // until the last segment ends, and both are stored with no loads in flight. The first
+  // segment runs in its own copy of the tile loop, free of the held registers.
   int b, ta, te;
+  if (!next_segment(a.seqlens, a.B, walk, b, ta, te)) return;
+  b = __builtin_amdgcn_readfirstlane(b);
+  BrAcc first;
+  br_segment(a, b, __builtin_amdgcn_readfirstlane(ta), __builtin_amdgcn_readfirstlane(te), j, lane, head_ok, ring,
+             full, first);
+  const int64_t slot0 = int64_t(g) + b;
+  const float l0 = halves_sum(first.l);
+  if (walk.cur >= walk.end) {
+    if (head_ok) br_store_partial(a, slot0, j, n, hh, first, l0);
+    return;
+  }
   while (next_segment(a.seqlens, a.B, walk, b, ta, te)) {
-    b = __builtin_amdgcn_readfirstlane(b);
-    ta = __builtin_amdgcn_readfirstlane(ta);
-    te = __builtin_amdgcn_readfirstlane(te);
-    const int L = scalar_read(a.seqlens + b);
-    // Query operands: latent K step ks covers channels 16*ks + 8*hh .. +8 of latent head j,
-    // RoPE K step rs channels 16*rs + 8*hh .. +8. Lanes past h load head 0 and are zeroed.
-    bf16x8 ql[8], qr[4];
-    {
-      const unsigned char* qn = a.q_nope + int64_t(b) * a.q_sb + int64_t(head_ok ? n : 0) * a.q_sh + 256 * j;
-      const unsigned char* qp = a.q_rope + int64_t(b) * a.qr_sb + int64_t(head_ok ? n : 0) * a.qr_sh;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) ql[ks] = *reinterpret_cast<const bf16x8*>(qn + (16 * ks + 8 * hh) * 2);
-#pragma unroll
-      for (int rs = 0; rs < 4; ++rs) qr[rs] = *reinterpret_cast<const bf16x8*>(qp + (16 * rs + 8 * hh) * 2);
-    }
-    floatx16 O[4] = {};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-
-    // The first kBranchStages-1 tiles go out while the queries are in flight; then wait for
-    // the queries only. The wait is a builtin so that the compiler, too, knows the query
-    // registers complete: it places no wait of its own on them inside the tile loop.
-    int issued = 0;
-#pragma unroll
-    for (int st = 0; st < kBranchStages - 1; ++st)
-      if (ta + st < te) {
-        br_issue_tile(a, b, L, ta + st, j, lane, ring + st * kBrTile, full);
-        ++issued;
-      }
-    if (issued == kBranchStages - 1)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm((kBranchStages - 1) * kBrLoads));
-    else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    if (!head_ok) {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) ql[ks] = bf16x8{};
-#pragma unroll
-      for (int rs = 0; rs < 4; ++rs) qr[rs] = bf16x8{};
-    }
-
-    for (int k = ta; k < te; ++k) {
-      const unsigned char* buf = ring + ((k - ta) % kBranchStages) * kBrTile;
-      if (k + kBranchStages - 1 < te) {
-        // Tile k+S-1 reuses tile k-1's buffer: this wave's reads of it have returned.
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        br_issue_tile(a, b, L, k + kBranchStages - 1, j, lane,
-                      ring + ((k - ta + kBranchStages - 1) % kBranchStages) * kBrTile, full);
-      }
-      br_wait_tile<kBranchStages>(min(kBranchStages - 1, te - 1 - k));
-
-      // S^T[token][head]: row n of the A operand is token n; chunk 2*ks + hh of latent row n
-      // sits at (2*ks + hh) ^ br_lat_swizzle(n), of RoPE row n at (2*rs + hh) ^ rope_swizzle(n).
-      floatx16 s = {};
-      {
-        const unsigned char* lrow = buf + n * kBrLatRow;
-        const unsigned char* rrow = buf + kBrLat + n * kBrRopeRow;
-        const int sw = br_lat_swizzle(n);
-        const int rsw = rope_swizzle<kBrRopeRow>(n);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 kk = *reinterpret_cast<const bf16x8*>(lrow + (((2 * ks + hh) ^ sw) << 4));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, ql[ks], s, 0, 0, 0);
-        }
-#pragma unroll
-        for (int rs = 0; rs < 4; ++rs) {
-          const bf16x8 kk = *reinterpret_cast<const bf16x8*>(rrow + (((2 * rs + hh) ^ rsw) << 4));
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qr[rs], s, 0, 0, 0);
-        }
-      }
-      const int n_valid = L - k * kTile;
-      if (n_valid < kTile) {
-        // Register r of lane half hh holds token 8*(r>>2) + 4*hh + (r&3).
-        const int lim = n_valid - 4 * hh;
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (8 * (r >> 2) + (r & 3) >= lim) s[r] = -INFINITY;
-      }
-      // Online softmax in log2 units: x = s * sm_scale * log2(e).
-      float mx = s[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = halves_max(mx);
-      const float mt = mx * a.c;
-      const bool raise = mt > m_run + kRescaleSlack;
-      if (__ballot(raise)) {
-        const float mnew = raise ? mt : m_run;
-        const float alpha = (mnew == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - mnew);
-        l_run *= alpha;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) O[mb] *= alpha;
-        m_run = mnew;
-      }
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.c, -m_run));
-        psum += s[r];
-      }
-      l_run += psum;
-
-      // O^T[channel][head] += V^T P^T: K step ks covers tokens 16*ks .. +16; lane (n, hh)
-      // takes token 16*ks + 8*(e>>2) + 4*hh + (e&3) as K index 8*hh + e. Output row m of
-      // M-block mb is channel 4*m + mb: each lane reads channels 4n .. 4n+3 (8 bytes).
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 v = __builtin_convertvector((floatx2{s[8 * ks + e], s[8 * ks + e + 1]}), bf16x2);
-          pb[e] = v[0];
-          pb[e + 1] = v[1];
-        }
-        u32x2 d[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tau = 16 * ks + 8 * (e >> 2) + 4 * hh + (e & 3);
-          d[e] = *reinterpret_cast<const u32x2*>(buf + tau * kBrLatRow + (((n >> 1) ^ br_lat_swizzle(tau)) << 4) +
-                                                 ((n & 1) << 3));
-        }
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const uint32_t sel = (mb & 1) ? 0x07060302u : 0x05040100u;
-          u32x4 av;
-#pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
-            const uint32_t lo = (mb < 2) ? d[2 * pp][0] : d[2 * pp][1];
-            const uint32_t hi = (mb < 2) ? d[2 * pp + 1][0] : d[2 * pp + 1][1];
-            av[pp] = __builtin_amdgcn_perm(hi, lo, sel);
-          }
-          O[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb, O[mb], 0, 0, 0);
-        }
-      }
-    }
-
-    // Partial of split g for sequence b, slot g + b: channel 32*gg + 16*hh + 4*i + mb of
-    // latent head j is O[mb][4*gg + i].
-    const int64_t pslot = int64_t(g) + b;
-    const float l_tot = halves_sum(l_run);
-    if (head_ok) {
-      float* dst = a.part_o + ((pslot * 4 + j) * a.h + n) * 128;
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<floatx4*>(dst + 32 * gg + 16 * hh + 4 * i) =
-              floatx4{O[0][4 * gg + i], O[1][4 * gg + i], O[2][4 * gg + i], O[3][4 * gg + i]};
-      if (hh == 0) {
-        float* ml = a.part_ml + ((pslot * 4 + j) * a.h + n) * 2;
-        ml[0] = m_run;
-        ml[1] = l_tot;
-      }
-    }
-    // Stores drained and LDS reads returned before the next segment reuses the ring (a
-    // builtin: the compiler's own wait tracking then starts the next segment clean).
+    // LDS reads returned before this segment's loads reuse the ring (a builtin: the
+    // compiler's own wait tracking then starts the segment clean).
     __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
     asm volatile("" ::: "memory");
+    b = __builtin_amdgcn_readfirstlane(b);
+    BrAcc cur;
+    br_segment(a, b, __builtin_amdgcn_readfirstlane(ta), __builtin_amdgcn_readfirstlane(te), j, lane, head_ok, ring,
+               full, cur);
+    const float l_tot = halves_sum(cur.l);
+    const bool last = walk.cur >= walk.end;
+    if (head_ok) {
+      if (last) br_store_partial(a, slot0, j, n, hh, first, l0);
+      br_store_partial(a, int64_t(g) + b, j, n, hh, cur, l_tot);
+    }
+    if (last) return;
   }
+  // Reached only if the walk ended on a segment short of the split's end.
+  if (head_ok) br_store_partial(a, slot0, j, n, hh, first, l0);
 }
 
 // ------------------------------------------------------------------ split-head decode (NB = 1, 2; bf16)

@@ -98,8 +98,10 @@ def test_edge_lengths_and_poisoned_padding(paged):
                 assert np.all(got[b] == 0.0)
 
 
-@pytest.mark.parametrize("h", [16, 8, 48, 64])
+@pytest.mark.parametrize("h", [1, 5, 8, 16, 33, 48, 64])
 def test_head_counts(h):
+    """Head counts below, between and at the 32-head blocks (1 and 5 leave most MFMA columns
+    empty; 33 puts one head in a second block)."""
     w = CONFIGS[2].replace(B=2, h=h, lengths=("list", (200, 45)))
     inp = make_inputs(w, seed=h)
     assert_parity(gpu_decode(inp), oracle.decode_inputs(inp), label=f"h={h}")
