@@ -41,7 +41,6 @@ namespace {
 // loads measured about 7 TB/s against about 6.1 TB/s for default-policy loads on MI355X.
 constexpr int kStreamPolicy = 2;
 
-
 // Wait until at most N of this wave's vector-memory operations are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -197,9 +196,7 @@ __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int head, boo
   }
 }
 
-// Source of 16-byte load `inst` (0 .. kInst-1) of a tile for lane `lane`: the
-// load fills LDS bytes [inst*1024 + 16*lane, +16) of the tile. Tokens past the
-// end of the sequence re-read its last token (valid data; their logits are masked).
+// Where tile `tile` of sequence b starts in the caches (through the block table when paged).
 struct TileRows {
   const unsigned char* lat;  // latent row of the tile's first token
   const unsigned char* rope; // RoPE row of the tile's first token
@@ -223,6 +220,9 @@ __device__ __forceinline__ TileRows tile_rows(const DecodeArgs& a, int b, int L,
   return r;
 }
 
+// Source of 16-byte load `inst` (0 .. kInst-1) of a tile for lane `lane`: the
+// load fills LDS bytes [inst*1024 + 16*lane, +16) of the tile. Tokens past the
+// end of the sequence re-read its last token (valid data; their logits are masked).
 template <typename T, int NB, int HB>
 __device__ __forceinline__ const unsigned char* load_src(const DecodeArgs& a, const TileRows& tr, int inst,
                                                          int lane) {

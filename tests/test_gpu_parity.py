@@ -82,6 +82,19 @@ def test_paged_every_form(name, page_size):
         assert_parity(gpu_decode(inp, splits), oracle.decode_inputs(inp), label=f"{name}/page={page_size}/splits={splits}", **tol)
 
 
+@pytest.mark.parametrize("cfg", [2, 5, 1])
+def test_mlra4_joint_rows(cfg):
+    """MLRA-4 with queries and cache stored as joint rows ([.., 576]: the four latent heads, then
+    RoPE), so every query and cache stride differs from the separate-tensor layout: contiguous and
+    paged bf16 (one wave per branch) and fp32 (whole tiles)."""
+    w = CONFIGS[cfg].replace(B=4, lengths=("list", (1, 70, 333, 64)), joint=True)
+    inp = make_inputs(w, seed=13, poison=True)
+    tol = dict(rel_l2=1e-4, max_abs=1e-3) if w.dtype == "f32" else {}
+    ref = oracle.decode_inputs(inp)
+    for splits in (0, 5):
+        assert_parity(gpu_decode(inp, splits), ref, label=f"joint cfg{cfg}/splits={splits}", **tol)
+
+
 EDGE_LENGTHS = (0, 1, 2, 31, 32, 33, 63, 64, 65, 95, 96, 97, 0, 128, 129, 5)
 
 
