@@ -24,7 +24,8 @@
 //                     heads, and every fp32 form.
 //   decode_hs_kernel  bf16 with one or two latent heads (MLA, MLRA-2), with the query
 //                     heads split across wave pairs.
-// Splitting is balanced over the flattened tiles of all sequences (the plan in mlra_device.h).
+// Splitting is balanced over the flattened tiles of all sequences (the plan in mlra_device.h),
+// and each XCD runs a contiguous run of splits (xcd_major_split).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -111,6 +112,17 @@ __device__ __forceinline__ Plan split_plan(const DecodeArgs& a) {
   Plan p = make_plan(a.seqlens, a.B, a.G_req);
   if (a.G_small > 0 && p.T < int64_t(kMinTilesPerSplit) * a.G_req) p.G = int(p.T < a.G_small ? p.T : a.G_small);
   return p;
+}
+
+// Split run by workgroup wg of the n active ones. Workgroups are dealt round-robin over the
+// 8 XCDs (wg % 8), so this gives XCD x a contiguous run of splits, and every XCD reads every
+// region of the caches. With split wg on workgroup wg, XCD x read the same eighth of every
+// sequence (the same 4 MiB-aligned blocks at B=32, L=32K), and on MI355X the odd XCDs then
+// finished 3-5 us after the even ones; with contiguous runs their finish times agree to 0.5 us.
+__device__ __forceinline__ int xcd_major_split(int wg, int n) {
+  const int x = wg & 7, i = wg >> 3;
+  const int q = n >> 3, r = n & 7;
+  return x * q + min(x, r) + i;
 }
 
 // Tile geometry. The LDS copy of a tile keeps the cache row order; within each row the
@@ -405,9 +417,9 @@ void decode_kernel(DecodeArgs a) {
   const bool head_ok = head < a.h;
 
   const Plan plan = split_plan(a);
-  const int g = blockIdx.x;
-  if (g == 0 && wave == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
-  if (g >= plan.G) return;
+  if (blockIdx.x == 0 && wave == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
+  if (int(blockIdx.x) >= plan.G) return;
+  const int g = xcd_major_split(blockIdx.x, plan.G);
   SegmentWalk walk = begin_walk(a.seqlens, a.B, g, plan);
 
   int b, ta, te;
@@ -817,9 +829,9 @@ void decode_branch_kernel(DecodeArgs a) {
   for (int i = 0; i < kBrLoads; ++i) full[i] = br_load_offset(a, i, j, lane, kTile - 1);
 
   const Plan plan = split_plan(a);
-  const int g = blockIdx.x;
-  if (g == 0 && j == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
-  if (g >= plan.G) return;
+  if (blockIdx.x == 0 && j == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
+  if (int(blockIdx.x) >= plan.G) return;
+  const int g = xcd_major_split(blockIdx.x, plan.G);
   SegmentWalk walk = begin_walk(a.seqlens, a.B, g, plan);
 
   // The split's partial for sequence b goes to slot g + b. A store issued while tiles stream
@@ -899,9 +911,9 @@ void decode_hs_kernel(DecodeArgs a) {
   const bool head_ok = head < a.h;
 
   const Plan plan = split_plan(a);
-  const int gsplit = blockIdx.x;
-  if (gsplit == 0 && wave == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
-  if (gsplit >= plan.G) return;
+  if (blockIdx.x == 0 && wave == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
+  if (int(blockIdx.x) >= plan.G) return;
+  const int gsplit = xcd_major_split(blockIdx.x, plan.G);
   SegmentWalk walk = begin_walk(a.seqlens, a.B, gsplit, plan);
 
   int b, ta, te;
