@@ -193,6 +193,24 @@ def cpu_baseline(inp, target_s):
                       f"tokens; median of {runs} run(s), {el:.1f} s each), scaled by token count to the full step"}
 
 
+def smi_clocks():
+    """Current clock levels as rocm-smi reports them, or None. Run before this process touches
+    the GPU: the tool is started as a child process."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        card = next(iter(json.loads(r.stdout).values()))
+        return {k: v for k, v in card.items() if any(c in k for c in ("sclk", "mclk", "fclk"))} or None
+    except Exception:
+        return None
+
+
+def device_info(torch, clocks):
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
+            "memory_GiB": round(pr.total_memory / 2 ** 30, 1), "clocks_before_run": clocks}
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -203,6 +221,7 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for {max(args.gpus, world)}); "
               f"the multi-GPU sharding of the decode is a design note, not a runnable path.", file=sys.stderr)
         sys.exit(2)
+    clocks = smi_clocks()
 
     import torch
     import long_context_decode_mlra_amd as mlra
@@ -377,6 +396,7 @@ def main():
         "absorb_query": absorb,
         "gqa_comparator": gqa,
         "cpu_baseline": None,
+        "device": device_info(torch, clocks),
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
