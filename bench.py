@@ -26,7 +26,9 @@ sys.path.insert(0, ROOT)
 METRIC = "MLRA-4 decode attn µs/step + achieved HBM TB/s (B=32, h=32, L=32K)"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense
-FLOP_PER_HEAD_TOKEN = 2 * (512 + 64) + 2 * 512     # QK (RoPE dot once) + PV, both forms
+def flop_per_head_token(w):
+    """QK over the latent and RoPE channels (the RoPE dot once per head) plus PV over the latent."""
+    return 2 * (w.NB * w.DL + w.DR) + 2 * w.NB * w.DL
 
 
 def parse():
@@ -36,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2000,
                     help="untimed steps first: on MI355X the whole-step time settles only after about 40 ms "
                          "of back-to-back work (about 200 steps at the headline shape), 25 %% above steady before")
-    ap.add_argument("--config", type=int, default=2, help="workload number (1-6); 2 is the headline")
+    ap.add_argument("--config", type=int, default=2, help="workload number (1-7); 2 is the headline")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = one split per resident workgroup slot")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -59,6 +61,8 @@ def attention_kernel_name(w):
     """The split-KV attention kernel the library launches for this workload."""
     if w.dtype == "bf16" and w.NB == 4 and w.h <= 32:
         return "decode_branch_kernel"
+    if w.dtype == "bf16" and w.NB == 1 and w.DL == 128:
+        return "decode_shard_kernel"
     if w.dtype == "bf16" and w.NB < 4:
         return "decode_hs_kernel"
     return "decode_kernel"
@@ -120,7 +124,7 @@ def record_traffic(fetch_csv, write_csv, args):
     w_scale = copy_bytes / (pick(wr, "copy_kernel") * 1024)
     w = CONFIGS[args.config]
     inp = make_inputs(w, seed=args.config)
-    attn = lambda d: next(v for k, v in d.items() if re.search(r"decode_(branch_|hs_)?kernel", k))
+    attn = lambda d: next(v for k, v in d.items() if re.search(r"decode_(branch_|hs_|shard_)?kernel", k))
     fetch = attn(f) * 1024 * f_scale
     write = attn(wr) * 1024 * w_scale
     ab = algorithmic_bytes(inp)
@@ -136,12 +140,16 @@ def record_traffic(fetch_csv, write_csv, args):
     print(json.dumps(rec))
 
 
-def gqa_leg(mlra, inp, args, stream, mlra_ms):
+def gqa_leg(mlra, inp, args, stream, mlra_ms, shard=False):
     """The GQA decode comparator at the pages' GQA shape (64 query heads over 8 KV heads of
-    128 channels) on the same batch and lengths as the MLRA workload; inputs drawn on the GPU."""
+    128 channels) on the same batch and lengths as the MLRA workload; inputs drawn on the GPU.
+    shard: one GPU's share of it under four-way tensor parallelism over heads (16 query heads
+    over 2 KV heads), to set beside the one-latent-head share of MLRA-4."""
     import torch
     from mlra_workloads import GQA_CONFIGS, make_gqa_inputs
     g = GQA_CONFIGS["gqa_bf16_b32_hq64_hkv8_L32k"].replace(B=len(inp.seqlens), lengths=("list", tuple(inp.seqlens.tolist())))
+    if shard:
+        g = g.replace(Hq=g.Hq // 4, Hkv=g.Hkv // 4)
     gi = make_gqa_inputs(g, seed=args.config, device="cuda")
     sl = gi.seqlens.to("cuda")
     dec = mlra.GqaDecoder(gi.q, gi.k_cache, gi.v_cache, seqlens=sl, sm_scale=g.sm_scale, max_seqlen=gi.max_seqlen)
@@ -156,7 +164,9 @@ def gqa_leg(mlra, inp, args, stream, mlra_ms):
     cb = gi.cache_bytes()
     del dec, gi
     torch.cuda.empty_cache()
-    return {"workload": f"gqa_bf16_b{g.B}_hq64_hkv8_d128 (lengths of this run)", "us_per_step": round(us, 2),
+    return {"workload": f"gqa_bf16_b{g.B}_hq{g.Hq}_hkv{g.Hkv}_d128 (lengths of this run"
+                        + ("; one GPU's share at four-way tensor parallelism)" if shard else ")"),
+            "us_per_step": round(us, 2),
             "cache_bytes": cb, "cache_GBps": round(cb / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(cb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "gqa_over_mlra_step_time": round(us / (mlra_ms * 1e3), 3),
@@ -193,22 +203,30 @@ def cpu_baseline(inp, target_s):
                       f"tokens; median of {runs} run(s), {el:.1f} s each), scaled by token count to the full step"}
 
 
-def smi_clocks():
-    """Current clock levels as rocm-smi reports them, or None. Run before this process touches
-    the GPU: the tool is started as a child process."""
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
-        card = next(iter(json.loads(r.stdout).values()))
-        return {k: v for k, v in card.items() if any(c in k for c in ("sclk", "mclk", "fclk"))} or None
-    except Exception:
-        return None
+def dpm_clocks():
+    """Clock levels from the amdgpu driver's sysfs tables (pp_dpm_sclk / _mclk / _fclk: one line
+    per level, the current one starred): the current and the highest level of each, per card.
+    Plain file reads, so they are safe in a process that has already touched the GPU."""
+    import glob
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card[0-9]*/device")):
+        card = {}
+        for kind in ("sclk", "mclk", "fclk"):
+            try:
+                lines = [l.strip() for l in open(os.path.join(dev, f"pp_dpm_{kind}")) if l.strip()]
+            except OSError:
+                continue
+            cur = [l.split(":", 1)[1].replace("*", "").strip() for l in lines if l.endswith("*")]
+            card[kind] = {"current": cur[0] if cur else None, "max": lines[-1].split(":", 1)[1].replace("*", "").strip()}
+        if card:
+            out[os.path.basename(os.path.dirname(dev))] = card
+    return out or None
 
 
-def device_info(torch, clocks):
+def device_info(torch):
     pr = torch.cuda.get_device_properties(0)
     return {"name": pr.name, "arch": getattr(pr, "gcnArchName", None), "compute_units": pr.multi_processor_count,
-            "memory_GiB": round(pr.total_memory / 2 ** 30, 1), "clocks_before_run": clocks}
+            "memory_GiB": round(pr.total_memory / 2 ** 30, 1), "dpm_clocks_after_run": dpm_clocks()}
 
 
 def main():
@@ -221,7 +239,6 @@ def main():
         print(f"bench.py: this build runs on one GPU only (asked for {max(args.gpus, world)}); "
               f"the multi-GPU sharding of the decode is a design note, not a runnable path.", file=sys.stderr)
         sys.exit(2)
-    clocks = smi_clocks()
 
     import torch
     import long_context_decode_mlra_amd as mlra
@@ -353,12 +370,12 @@ def main():
                   "achieved_GBps": round(a_bytes / (a_us * 1e-6) / 1e9, 1)}
     gqa = None
     if not args.no_gqa and w.dtype == "bf16" and w.page_size == 0:
-        gqa = gqa_leg(mlra, inp, args, stream, ms_per_step)
+        gqa = gqa_leg(mlra, inp, args, stream, ms_per_step, shard=(w.NB == 1 and w.DL == 128))
     dk = sorted(e[0].elapsed_time(e[1]) for e in evs)
 
     ab = algorithmic_bytes(inp)
     tokens = inp.total_tokens
-    flops = FLOP_PER_HEAD_TOKEN * w.h * tokens + 2 * len(inp.seqlens) * w.h * 512 * w.DV
+    flops = flop_per_head_token(w) * w.h * tokens + 2 * len(inp.seqlens) * w.h * w.NB * w.DL * w.DV
     us = ms_per_step * 1e3
     achieved = ab["attention"] / (dk_mean * 1e-3) / 1e9
     trec = traffic_record(w.name)
@@ -396,7 +413,7 @@ def main():
         "absorb_query": absorb,
         "gqa_comparator": gqa,
         "cpu_baseline": None,
-        "device": device_info(torch, clocks),
+        "device": device_info(torch),
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)

@@ -21,6 +21,13 @@
  * MLA: NB = 1, d_latent = 512, out_scale = 1. Every form caches
  * NB*d_latent + d_rope = 512 + 64 elements per token.
  *
+ * The shard form, NB = 1 and d_latent = 128 (bf16, at most 32 query heads), is
+ * one GPU's share of MLRA-4 when its latent heads are spread over four GPUs
+ * ("Key Contributions" #2): latent head j plus the RoPE key, 128 + 64 elements
+ * per token, with W_UV[j] and out_scale = 1/2. The sum of the four shares'
+ * outputs is the MLRA-4 output; that sum (a cross-GPU all-reduce) is not part
+ * of this library.
+ *
  * Threading and streams: every call that takes a stream only enqueues work
  * on that HIP stream (hipStream_t passed as void*, NULL = the null stream) and
  * returns without synchronising. Device-side faults surface at the caller's
@@ -70,7 +77,7 @@ typedef struct mlra_decode_params {
   int32_t batch;             /* B >= 0 sequences, one new token each */
   int32_t num_heads;         /* h, 1..MLRA_MAX_HEADS */
   int32_t num_branches;      /* NB: 4 (MLRA-4), 2 (MLRA-2) or 1 (absorbed MLA) */
-  int32_t d_latent;          /* channels per latent head; must equal 512 / NB */
+  int32_t d_latent;          /* channels per latent head: 512 / NB, or 128 with NB = 1 (the shard form) */
   int32_t d_rope;            /* RoPE key channels; must be 64 */
   int32_t d_v;               /* output channels per head; must be 128 */
   int32_t dtype;             /* MLRA_BF16 or MLRA_F32 */
@@ -78,9 +85,11 @@ typedef struct mlra_decode_params {
                                 block_table required, tokens per page, a multiple of 32 */
   int32_t max_seqlen;        /* >= every seqlens[b]; contiguous cache: rows reserved per sequence */
   int32_t max_pages_per_seq; /* paged cache: row stride of block_table (>= ceil(max_seqlen/page_size)) */
-  int32_t num_splits;        /* decode workgroups, one split each; 0 = one per resident slot on the
-                                device, and then, when the batch's tiles would give fewer than 56
-                                per split, the kernel runs one split per compute unit instead */
+  int32_t num_splits;        /* token splits; one workgroup each (the shard form: four per workgroup,
+                                one per wave). 0 = one per resident slot on the device (the shard
+                                form: four per resident workgroup), and then, for the two-per-CU
+                                kernels, when the batch's tiles would give fewer than 56 per split,
+                                one split per compute unit instead */
   int32_t reserved;          /* must be 0 */
   int64_t q_stride_b, q_stride_h;   /* q_nope strides in elements; the NB*d_latent row is contiguous */
   int64_t qr_stride_b, qr_stride_h; /* q_rope strides in elements; the d_rope row is contiguous */
@@ -99,9 +108,10 @@ const char* mlra_last_error(void);
 /* Host-only validation of `p` (no HIP call, no device). Returns 0 or a negative code. */
 int mlra_check_params(const mlra_decode_params* p);
 
-/* Decode workgroups a call with `p` launches: p->num_splits if positive, else
- * (compute units of the current device) x (resident workgroups per unit).
- * The second case queries the current HIP device. Returns 0 or a negative code. */
+/* Token splits of a call with `p`: p->num_splits if positive, else (compute
+ * units of the current device) x (resident workgroups per unit), times four in
+ * the shard form (a split per wave). The second case queries the current HIP
+ * device. Returns 0 or a negative code. */
 int mlra_decode_num_splits(const mlra_decode_params* p, int32_t* num_splits);
 
 /* Bytes of workspace mlra_decode needs for `p` (uses mlra_decode_num_splits). */

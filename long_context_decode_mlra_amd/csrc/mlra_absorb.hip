@@ -21,7 +21,7 @@ struct AbsorbArgs {
   const unsigned char* q_pre;
   const float* W_UK;  // [NB][h][DL][128]
   unsigned char* q_nope;
-  int B, h, NB;
+  int B, h, NB, DL;             // DL: channels per latent head
   int64_t qp_sb, qp_sh, qp_sj;  // bytes
   int64_t qn_sb, qn_sh;         // bytes
 };
@@ -55,7 +55,7 @@ __global__ __launch_bounds__(64) void absorb_kernel(AbsorbArgs a) {
   const int i = blockIdx.x;
   const int rb = blockIdx.y;
   const int grp = blockIdx.z;
-  const int DL = kLatentTotal / a.NB;
+  const int DL = a.DL;
   const int j = (rb * kAbsorbRows) / DL;
   const int c0 = (rb * kAbsorbRows) % DL;
   const int b0 = grp * kAbsorbSeqs;
@@ -123,12 +123,14 @@ extern "C" int mlra_absorb_query(const void* q_pre, const float* W_UK, void* q_n
   a.B = p->batch;
   a.h = p->num_heads;
   a.NB = p->num_branches;
+  a.DL = p->d_latent;
   a.qp_sb = qpre_stride_b * esz;
   a.qp_sh = qpre_stride_h * esz;
   a.qp_sj = qpre_stride_j * esz;
   a.qn_sb = p->q_stride_b * esz;
   a.qn_sh = p->q_stride_h * esz;
-  const dim3 grid(p->num_heads, kLatentTotal / kAbsorbRows, (p->batch + kAbsorbSeqs - 1) / kAbsorbSeqs);
+  static_assert(kShardLatent % kAbsorbRows == 0, "latent heads are whole row blocks");
+  const dim3 grid(p->num_heads, latent_total(*p) / kAbsorbRows, (p->batch + kAbsorbSeqs - 1) / kAbsorbSeqs);
   if (p->dtype == MLRA_BF16)
     hipLaunchKernelGGL(absorb_kernel<__bf16>, grid, dim3(64), 0, static_cast<hipStream_t>(stream), a);
   else

@@ -24,6 +24,8 @@
 //                     heads, and every fp32 form.
 //   decode_hs_kernel  bf16 with one or two latent heads (MLA, MLRA-2), with the query
 //                     heads split across wave pairs.
+//   decode_shard_kernel  the shard form, one latent head of 128 channels (bf16, up to 32 query
+//                     heads): the branch-wave computation with a split per wave.
 // Splitting is balanced over the flattened tiles of all sequences (the plan in mlra_device.h),
 // and each XCD runs a contiguous run of splits (xcd_major_split).
 #include <hip/hip_runtime.h>
@@ -796,9 +798,11 @@ __device__ __forceinline__ void br_segment(const DecodeArgs& a, int b, int ta, i
   }
 }
 
+// The partial of latent head j (of NB) at slot pslot.
+template <int NB>
 __device__ __forceinline__ void br_store_partial(const DecodeArgs& a, int64_t pslot, int j, int n, int hh,
                                                  const BrAcc& acc, float l_tot) {
-  float* dst = a.part_o + ((pslot * 4 + j) * a.h + n) * 128;
+  float* dst = a.part_o + ((pslot * NB + j) * a.h + n) * 128;
 #pragma unroll
   for (int gg = 0; gg < 4; ++gg)
 #pragma unroll
@@ -806,39 +810,24 @@ __device__ __forceinline__ void br_store_partial(const DecodeArgs& a, int64_t ps
       *reinterpret_cast<floatx4*>(dst + 32 * gg + 16 * hh + 4 * i) =
           floatx4{acc.O[0][4 * gg + i], acc.O[1][4 * gg + i], acc.O[2][4 * gg + i], acc.O[3][4 * gg + i]};
   if (hh == 0) {
-    float* ml = a.part_ml + ((pslot * 4 + j) * a.h + n) * 2;
+    float* ml = a.part_ml + ((pslot * NB + j) * a.h + n) * 2;
     ml[0] = acc.m;
     ml[1] = l_tot;
   }
 }
 
-// Launch bounds allow one wave per SIMD (the LDS ring admits no more). Built with the MFMA
-// VGPR form (-amdgpu-mfma-vgpr-form): otherwise the compiler keeps the accumulators in AGPRs
-// and copies them to and from VGPRs every tile.
-__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
-void decode_branch_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kBranchStages * kBrTile];
-  const int lane = threadIdx.x & 63;
-  const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // latent head of this wave
-  const int n = lane & 31;  // query head (MFMA column) and token row of the A operand
+// Split g of latent head j (of NB) by one wave, through the ring `ring`: the partial for
+// sequence b goes to slot g + b. A store issued while tiles stream in delays every later tile
+// wait (the vector-memory counter retires loads and stores in order), so when a split spans
+// sequences the first segment's partial stays in registers until the last segment ends, and
+// both are stored with no loads in flight. The first segment runs in its own copy of the tile
+// loop, free of the held registers.
+template <int NB>
+__device__ __forceinline__ void br_run_split(const DecodeArgs& a, const Plan& plan, int g, int j, int lane,
+                                             bool head_ok, unsigned char* ring, const uint32_t (&full)[kBrLoads]) {
+  const int n = lane & 31;
   const int hh = lane >> 5;
-  const bool head_ok = n < a.h;
-  unsigned char* ring = smem + j * (kBranchStages * kBrTile);
-  uint32_t full[kBrLoads];
-#pragma unroll
-  for (int i = 0; i < kBrLoads; ++i) full[i] = br_load_offset(a, i, j, lane, kTile - 1);
-
-  const Plan plan = split_plan(a);
-  if (blockIdx.x == 0 && j == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
-  if (int(blockIdx.x) >= plan.G) return;
-  const int g = xcd_major_split(blockIdx.x, plan.G);
   SegmentWalk walk = begin_walk(a.seqlens, a.B, g, plan);
-
-  // The split's partial for sequence b goes to slot g + b. A store issued while tiles stream
-  // in delays every later tile wait (the vector-memory counter retires loads and stores in
-  // order), so when a split spans sequences the first segment's partial stays in registers
-  // until the last segment ends, and both are stored with no loads in flight. The first
-  // segment runs in its own copy of the tile loop, free of the held registers.
   int b, ta, te;
   if (!next_segment(a.seqlens, a.B, walk, b, ta, te)) return;
   b = __builtin_amdgcn_readfirstlane(b);
@@ -848,7 +837,7 @@ void decode_branch_kernel(DecodeArgs a) {
   const int64_t slot0 = int64_t(g) + b;
   const float l0 = halves_sum(first.l);
   if (walk.cur >= walk.end) {
-    if (head_ok) br_store_partial(a, slot0, j, n, hh, first, l0);
+    if (head_ok) br_store_partial<NB>(a, slot0, j, n, hh, first, l0);
     return;
   }
   while (next_segment(a.seqlens, a.B, walk, b, ta, te)) {
@@ -863,13 +852,60 @@ void decode_branch_kernel(DecodeArgs a) {
     const float l_tot = halves_sum(cur.l);
     const bool last = walk.cur >= walk.end;
     if (head_ok) {
-      if (last) br_store_partial(a, slot0, j, n, hh, first, l0);
-      br_store_partial(a, int64_t(g) + b, j, n, hh, cur, l_tot);
+      if (last) br_store_partial<NB>(a, slot0, j, n, hh, first, l0);
+      br_store_partial<NB>(a, int64_t(g) + b, j, n, hh, cur, l_tot);
     }
     if (last) return;
   }
   // Reached only if the walk ended on a segment short of the split's end.
-  if (head_ok) br_store_partial(a, slot0, j, n, hh, first, l0);
+  if (head_ok) br_store_partial<NB>(a, slot0, j, n, hh, first, l0);
+}
+
+// Launch bounds allow one wave per SIMD (the LDS ring admits no more). Built with the MFMA
+// VGPR form (-amdgpu-mfma-vgpr-form): otherwise the compiler keeps the accumulators in AGPRs
+// and copies them to and from VGPRs every tile.
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void decode_branch_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kBranchStages * kBrTile];
+  const int lane = threadIdx.x & 63;
+  const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // latent head of this wave
+  const bool head_ok = (lane & 31) < a.h;  // lane's query head (MFMA column)
+  unsigned char* ring = smem + j * (kBranchStages * kBrTile);
+  uint32_t full[kBrLoads];
+#pragma unroll
+  for (int i = 0; i < kBrLoads; ++i) full[i] = br_load_offset(a, i, j, lane, kTile - 1);
+
+  const Plan plan = split_plan(a);
+  if (blockIdx.x == 0 && j == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
+  if (int(blockIdx.x) >= plan.G) return;
+  br_run_split<4>(a, plan, xcd_major_split(blockIdx.x, plan.G), j, lane, head_ok, ring, full);
+}
+
+// ------------------------------------------------------------------ one latent head (shard form)
+//
+// The shard form caches one latent head of 128 channels plus the RoPE rows: one GPU's share of
+// MLRA-4 when the latent heads are spread over four GPUs ("Key Contributions" #2; the branch
+// sum then becomes a sum across GPUs). Each wave of a workgroup runs a split of its own, as one
+// branch wave of decode_branch_kernel runs its split, so a workgroup runs four consecutive
+// splits and the split count is four per resident workgroup.
+__global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
+void decode_shard_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * kBranchStages * kBrTile];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool head_ok = (lane & 31) < a.h;
+  unsigned char* ring = smem + wave * (kBranchStages * kBrTile);
+  uint32_t full[kBrLoads];
+#pragma unroll
+  for (int i = 0; i < kBrLoads; ++i) full[i] = br_load_offset(a, i, 0, lane, kTile - 1);
+
+  const Plan plan = split_plan(a);
+  if (blockIdx.x == 0 && wave == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
+  const int wgs = (plan.G + 3) / 4;  // workgroups holding at least one split
+  if (int(blockIdx.x) >= wgs) return;
+  const int g = 4 * xcd_major_split(blockIdx.x, wgs) + wave;
+  if (g >= plan.G) return;
+  br_run_split<1>(a, plan, g, 0, lane, head_ok, ring, full);
 }
 
 // ------------------------------------------------------------------ split-head decode (NB = 1, 2; bf16)
@@ -1087,9 +1123,11 @@ void decode_hs_kernel(DecodeArgs a) {
 
 using DecodeFn = void (*)(DecodeArgs);
 
-DecodeFn pick_decode(int dtype, int nb, int hb) {
+DecodeFn pick_decode(int dtype, int nb, int dl, int hb) {
 #define MLRA_PICK(T, NB_)                                                        \
   if (nb == NB_) return hb == 1 ? decode_kernel<T, NB_, 1> : decode_kernel<T, NB_, 2>;
+  if (dl * nb != kLatentTotal) return (dtype == MLRA_BF16 && nb == 1 && dl == kShardLatent && hb == 1)
+                                          ? decode_shard_kernel : nullptr;
   if (dtype == MLRA_BF16) {
     if (nb == 4) return hb == 1 ? decode_branch_kernel : decode_kernel<__bf16, 4, 2>;
     if (nb == 2) return hb == 1 ? decode_hs_kernel<2, 1> : decode_hs_kernel<2, 2>;
@@ -1107,13 +1145,13 @@ DecodeFn pick_decode(int dtype, int nb, int hb) {
 // receives the compute units of the device.
 int resident_splits(const mlra_decode_params& p, int32_t* out, int* cus_out = nullptr) {
   static std::mutex mu;
-  static int cache[64][2][3][2];  // device, dtype, log2 NB, HB-1
+  static int cache[64][2][4][2];  // device, dtype, log2 NB (3: the shard form), HB-1
   static int cus_cache[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   const int hb = head_blocks(p.num_heads);
-  const int nbi = p.num_branches == 4 ? 2 : p.num_branches == 2 ? 1 : 0;
+  const int nbi = is_shard(p) ? 3 : p.num_branches == 4 ? 2 : p.num_branches == 2 ? 1 : 0;
   if (dev >= 0 && dev < 64) {
     std::lock_guard<std::mutex> lk(mu);
     if (cache[dev][p.dtype][nbi][hb - 1] > 0) {
@@ -1126,11 +1164,12 @@ int resident_splits(const mlra_decode_params& p, int32_t* out, int* cus_out = nu
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
   int per_cu = 0;
-  const void* kernel = reinterpret_cast<const void*>(pick_decode(p.dtype, p.num_branches, hb));
+  const void* kernel = reinterpret_cast<const void*>(pick_decode(p.dtype, p.num_branches, p.d_latent, hb));
+  if (!kernel) return set_error(MLRA_ERR_UNSUPPORTED, "no decode kernel for this configuration");
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256 * hb, 0);
   if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
   if (per_cu < 1) per_cu = 1;
-  const int n = cus * per_cu;
+  const int n = cus * per_cu * (is_shard(p) ? 4 : 1);  // the shard kernel runs a split per wave
   if (dev >= 0 && dev < 64) {
     std::lock_guard<std::mutex> lk(mu);
     cache[dev][p.dtype][nbi][hb - 1] = n;
@@ -1203,7 +1242,7 @@ extern "C" int mlra_decode_splitkv(const void* q_nope, const void* q_rope, const
     int cus = 0;
     rc = resident_splits(*p, &resident, &cus);
     if (rc) return rc;
-    if (cus > 0 && G >= 2 * cus) a.G_small = cus;
+    if (cus > 0 && G >= 2 * cus && !is_shard(*p)) a.G_small = cus;
   }
   a.page_size = p->page_size > 0 ? p->page_size : 1;
   a.max_seqlen = p->max_seqlen;
@@ -1217,9 +1256,10 @@ extern "C" int mlra_decode_splitkv(const void* q_nope, const void* q_rope, const
   a.c = p->sm_scale * kLog2e;
 
   const int hb = head_blocks(p->num_heads);
-  DecodeFn fn = pick_decode(p->dtype, p->num_branches, hb);
+  DecodeFn fn = pick_decode(p->dtype, p->num_branches, p->d_latent, hb);
   if (!fn) return set_error(MLRA_ERR_UNSUPPORTED, "no decode kernel for this configuration");
-  hipLaunchKernelGGL(fn, dim3(G), dim3(256 * hb), 0, static_cast<hipStream_t>(stream), a);
+  const int wgs = is_shard(*p) ? (G + 3) / 4 : G;  // the shard kernel runs four splits per workgroup
+  hipLaunchKernelGGL(fn, dim3(wgs), dim3(256 * hb), 0, static_cast<hipStream_t>(stream), a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "decode kernel launch");
   return MLRA_OK;

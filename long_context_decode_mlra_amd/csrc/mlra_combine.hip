@@ -14,8 +14,8 @@ namespace {
 
 // ------------------------------------------------------------------ combine kernel
 //
-// One workgroup per (query head i, block q of kCombBlock of the 512 latent channels, group of
-// up to 32 sequences). Block q lies in latent head j = q*kCombBlock / d_latent, channels
+// One workgroup per (query head i, block q of kCombBlock of the NB * d_latent latent channels
+// (512, or 128 in the shard form), group of up to 32 sequences). Block q lies in latent head j = q*kCombBlock / d_latent, channels
 // c0..c0+kCombBlock-1 of it, c0 = q*kCombBlock % d_latent.
 //  1. merge:   obar[b][k] = sum_s 2^{m_s-M} O_s[c0+k] / sum_s 2^{m_s-M} l_s over the splits
 //              s holding part of sequence b (slots g + b, g in [g_first, g_last]), into LDS.
@@ -32,12 +32,12 @@ struct CombineArgs {
   const float* part_ml;
   const int64_t* prefix;
   const float* W_UV;
-  float* ypart;    // [groups][h][kCombBlocks][32][128]
+  float* ypart;    // [groups][h][nblk][32][128]
   int B, h;
+  int nblk;        // kCombBlock-channel blocks of the NB * d_latent latent channels
 };
 
 constexpr int kCombSeqs = 32;
-constexpr int kCombBlocks = kLatentTotal / kCombBlock;
 constexpr int kCombTPS = kCombBlock / 16;  // merge threads per sequence, 4 channel quads each
 
 struct MergeState {
@@ -64,9 +64,8 @@ __device__ __forceinline__ void merge_in(MergeState& st, float m, float l, const
 // Workgroup barrier that orders LDS only (the W_UV loads issued first stay in flight).
 __device__ __forceinline__ void comb_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int NB>
+template <int NB, int DL>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
-  constexpr int DL = kLatentTotal / NB;
   constexpr int kBatch = 4;  // slots loaded together
   constexpr int kSteps = kCombBlock / 2;  // K steps of the 32x32x2 MFMA
   __shared__ float ob[kCombBlock][kCombSeqs];  // merged block, k-major: ob[k][b]
@@ -181,7 +180,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 #pragma unroll
   for (int kb = 0; kb < kSteps; ++kb) y = __builtin_amdgcn_mfma_f32_32x32x2f32(ob[2 * kb + hh][n], wv[kb], y, 0, 0, 0);
 
-  float* yq = a.ypart + ((int64_t(grp) * a.h + i) * kCombBlocks + q) * (kCombSeqs * kDV);
+  float* yq = a.ypart + ((int64_t(grp) * a.h + i) * a.nblk + q) * (kCombSeqs * kDV);
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) yq[(8 * (rr >> 2) + 4 * hh + (rr & 3)) * kDV + 32 * wave + n] = y[rr];
 }
@@ -194,6 +193,7 @@ struct FinalizeArgs {
   float out_scale;
 };
 
+template <int NBLK>
 __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
   const int64_t n4 = int64_t(a.B) * a.h * (kDV / 4);
   const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -204,22 +204,26 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
   const int b = int(bi / a.h);
   const int grp = b / kCombSeqs, bl = b % kCombSeqs;
   const floatx4* y = reinterpret_cast<const floatx4*>(
-                         a.ypart + ((int64_t(grp) * a.h + i) * kCombBlocks) * (kCombSeqs * kDV) + bl * kDV) + d4;
+                         a.ypart + ((int64_t(grp) * a.h + i) * NBLK) * (kCombSeqs * kDV) + bl * kDV) + d4;
   constexpr int kBlk = kCombSeqs * kDV / 4;
   floatx4 v = y[0];
 #pragma unroll
-  for (int qq = 1; qq < kCombBlocks; ++qq) v += y[qq * kBlk];
+  for (int qq = 1; qq < NBLK; ++qq) v += y[qq * kBlk];
   reinterpret_cast<floatx4*>(a.out)[idx] = a.out_scale * v;
 }
 
 using CombineFn = void (*)(CombineArgs);
+using FinalizeFn = void (*)(FinalizeArgs);
 
-CombineFn pick_combine(int nb) {
-  switch (nb) {
-    case 4: return combine_kernel<4>;
-    case 2: return combine_kernel<2>;
-    default: return combine_kernel<1>;
-  }
+CombineFn pick_combine(int nb, int dl) {
+  if (nb == 4) return combine_kernel<4, 128>;
+  if (nb == 2) return combine_kernel<2, 256>;
+  return dl == kShardLatent ? combine_kernel<1, kShardLatent> : combine_kernel<1, 512>;
+}
+
+FinalizeFn pick_finalize(int nblk) {
+  return nblk == kShardLatent / kCombBlock ? finalize_kernel<kShardLatent / kCombBlock>
+                                           : finalize_kernel<kLatentTotal / kCombBlock>;
 }
 
 }  // namespace
@@ -247,8 +251,10 @@ extern "C" int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, fl
   c.ypart = reinterpret_cast<float*>(ws + lay.ypart_off);
   c.B = p->batch;
   c.h = p->num_heads;
-  const dim3 grid(p->num_heads, kCombBlocks, (p->batch + kCombSeqs - 1) / kCombSeqs);
-  hipLaunchKernelGGL(pick_combine(p->num_branches), grid, dim3(256), 0, static_cast<hipStream_t>(stream), c);
+  c.nblk = latent_total(*p) / kCombBlock;
+  const dim3 grid(p->num_heads, c.nblk, (p->batch + kCombSeqs - 1) / kCombSeqs);
+  hipLaunchKernelGGL(pick_combine(p->num_branches, p->d_latent), grid, dim3(256), 0,
+                     static_cast<hipStream_t>(stream), c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
   FinalizeArgs f;
@@ -258,7 +264,7 @@ extern "C" int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, fl
   f.h = p->num_heads;
   f.out_scale = p->out_scale;
   const int64_t n4 = int64_t(p->batch) * p->num_heads * (kDV / 4);
-  hipLaunchKernelGGL(finalize_kernel, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0,
+  hipLaunchKernelGGL(pick_finalize(c.nblk), dim3(unsigned((n4 + 255) / 256)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), f);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "finalize kernel launch");

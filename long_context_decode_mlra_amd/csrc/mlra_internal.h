@@ -11,7 +11,8 @@ namespace mlra {
 
 constexpr int kTile = MLRA_TILE_TOKENS;   // tokens per tile of the split-KV stream
 constexpr int kHeadBlock = 32;            // query heads per MFMA column block
-constexpr int kLatentTotal = 512;         // NB * d_latent in every supported form
+constexpr int kLatentTotal = 512;         // NB * d_latent of the whole-cache forms (MLRA-4, MLRA-2, MLA)
+constexpr int kShardLatent = 128;         // d_latent of the one-latent-head shard form (NB = 1)
 constexpr int kDRope = 64;
 constexpr int kDV = 128;
 #ifndef MLRA_COMBINE_BLOCK
@@ -19,12 +20,19 @@ constexpr int kDV = 128;
 #endif
 constexpr int kCombBlock = MLRA_COMBINE_BLOCK;  // latent channels per combine workgroup (64 or 128)
 
+// Latent channels per cached token: 512, or 128 for the shard form.
+inline int latent_total(const mlra_decode_params& p) { return p.num_branches * p.d_latent; }
+
+// The shard form: one latent head of 128 channels (one GPU's share of MLRA-4 split by latent head).
+inline bool is_shard(const mlra_decode_params& p) { return p.num_branches == 1 && p.d_latent == kShardLatent; }
+
 // Workspace of one decode call:
 //   part_o  fp32 [slots][NB][h][d_latent]  unnormalised output of one split for one sequence
 //                                          (slot = split + sequence)
 //   part_ml fp32 [slots][NB][h][2]         (running max in log2 units, running sum)
 //   prefix  int64 [B + 3]                  first tile of each sequence, then T (total tiles), T, G
-//   ypart   fp32 [groups][h][512/kCombBlock][32][d_v]  projected channel blocks of up to 32 sequences
+//   ypart   fp32 [groups][h][NB*d_latent/kCombBlock][32][d_v]  projected channel blocks of up to
+//                                          32 sequences
 // groups = ceil(B / 32).
 struct WorkspaceLayout {
   int64_t slots = 0;

@@ -30,14 +30,14 @@ WorkspaceLayout workspace_layout(const mlra_decode_params& p, int32_t num_splits
   WorkspaceLayout w;
   // Split g writes at most one partial per sequence it touches, at slot g + b; g + b < G + B.
   w.slots = int64_t(num_splits) + int64_t(p.batch);
-  const size_t per_slot_o = size_t(p.num_heads) * kLatentTotal * sizeof(float);
+  const size_t per_slot_o = size_t(p.num_heads) * latent_total(p) * sizeof(float);
   const size_t per_slot_ml = size_t(p.num_branches) * size_t(p.num_heads) * 2 * sizeof(float);
   w.part_o_off = 0;
   w.part_ml_off = align256(size_t(w.slots) * per_slot_o);
   w.prefix_off = align256(w.part_ml_off + size_t(w.slots) * per_slot_ml);
   const size_t groups = (size_t(p.batch) + 31) / 32;
   w.ypart_off = align256(w.prefix_off + (size_t(p.batch) + 3) * sizeof(int64_t));
-  w.total = align256(w.ypart_off + groups * size_t(p.num_heads) * (kLatentTotal / kCombBlock) * 32 * kDV *
+  w.total = align256(w.ypart_off + groups * size_t(p.num_heads) * (latent_total(p) / kCombBlock) * 32 * kDV *
                                        sizeof(float));
   return w;
 }
@@ -105,9 +105,14 @@ extern "C" int mlra_check_params(const mlra_decode_params* p) {
     return set_error(MLRA_ERR_UNSUPPORTED, "num_heads must be in [1, %d] (got %d)", MLRA_MAX_HEADS, p->num_heads);
   if (p->num_branches != 1 && p->num_branches != 2 && p->num_branches != 4)
     return set_error(MLRA_ERR_UNSUPPORTED, "num_branches must be 1, 2 or 4 (got %d)", p->num_branches);
-  if (p->d_latent * p->num_branches != kLatentTotal)
-    return set_error(MLRA_ERR_UNSUPPORTED, "d_latent must be 512 / num_branches = %d (got %d)",
+  if (p->d_latent * p->num_branches != kLatentTotal && !is_shard(*p))
+    return set_error(MLRA_ERR_UNSUPPORTED, "d_latent must be 512 / num_branches = %d, or 128 with one branch (got %d)",
                      kLatentTotal / p->num_branches, p->d_latent);
+  if (is_shard(*p) && p->dtype != MLRA_BF16)
+    return set_error(MLRA_ERR_UNSUPPORTED, "the one-latent-head shard form (d_latent 128) takes bf16 only");
+  if (is_shard(*p) && p->num_heads > kHeadBlock)
+    return set_error(MLRA_ERR_UNSUPPORTED, "the one-latent-head shard form takes at most %d query heads (got %d)",
+                     kHeadBlock, p->num_heads);
   if (p->d_rope != kDRope) return set_error(MLRA_ERR_UNSUPPORTED, "d_rope must be 64 (got %d)", p->d_rope);
   if (p->d_v != kDV) return set_error(MLRA_ERR_UNSUPPORTED, "d_v must be 128 (got %d)", p->d_v);
   if (p->dtype != MLRA_BF16 && p->dtype != MLRA_F32)

@@ -90,6 +90,11 @@ CONFIGS = {
                 lengths=("loguniform", 1024, 65536), page_size=64),
     # MLRA-2 (two latent heads of 256 channels, rescale 1/sqrt(2)) at the headline shape.
     6: Workload("mlra2_bf16_b32_h32_L32k", "bf16", B=32, h=32, NB=2, DL=256, lengths=("fixed", 32768)),
+    # One GPU's share of workload 2 when its four latent heads are spread over four GPUs: one
+    # latent head of 128 channels plus the replicated RoPE keys, one joint 192-wide row per token,
+    # the MLRA-4 rescale 1/2 applied before the cross-GPU sum.
+    7: Workload("mlra4_shard_bf16_b32_h32_L32k", "bf16", B=32, h=32, NB=1, DL=128, lengths=("fixed", 32768),
+                rope_std=math.sqrt(1536.0 / 512.0), out_scale=0.5, joint=True),
 }
 
 

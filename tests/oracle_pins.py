@@ -19,7 +19,8 @@ Sources of truth (page "Multi-Head Low-Rank Attention", ai.info summary):
   one half of MLA over the stacked latent: the block decomposition of
   "Key Contributions" #1 and the 1/2 rescale of #3);
 * invariants: branch softmaxes are separate (MLRA-4 differs from 1/2 MLA on
-  generic data, "Methodology in Plain English" 2nd paragraph), paged equals
+  generic data, "Methodology in Plain English" 2nd paragraph), the latent heads
+  decoded apart sum to the whole ("Key Contributions" #2), paged equals
   contiguous, token order does not matter, adding a constant to all logits
   of a head does not change its output, an empty sequence gives zero.
 """
@@ -182,6 +183,19 @@ def pin_shared_rope_half_mla(decode):
     np.testing.assert_allclose(mlra, 0.5 * mla, rtol=1e-12, atol=1e-13)
 
 
+def pin_shards_sum_to_whole(decode):
+    """The latent heads can be decoded apart (one per GPU in the pages' tensor-parallel layout,
+    "Key Contributions" #2): decoding each latent head alone, with its own W_UV block and the
+    same rescale, and summing the NB results gives the NB-head output (exact)."""
+    rng = np.random.default_rng(16)
+    c = tiny_case(rng, B=2, h=3, NB=4, DL=4, DR=3, DV=2, Ls=(9, 3), scale=1.5)
+    whole = _call(decode, c, sm_scale=0.7, out_scale=0.5)
+    parts = [decode(c["q_nope"][:, :, j:j + 1], c["q_rope"], c["latent"][:, j:j + 1], c["rope"],
+                    c["W_UV"][j:j + 1], c["seqlens"], sm_scale=0.7, out_scale=0.5, max_seqlen=c["max_seqlen"])
+             for j in range(4)]
+    np.testing.assert_allclose(sum(parts), whole, rtol=1e-12, atol=1e-13)
+
+
 def pin_branches_separate(decode):
     """Generic q_nope: per-branch softmaxes are not the MLA softmax; the results must differ."""
     rng = np.random.default_rng(14)
@@ -315,5 +329,5 @@ def pin_absorb_is_unabsorbed_attention(decode, absorb=None):
 
 
 ALL_PINS = [pin_golden, pin_unabsorbed_bruteforce, pin_sdpa_library, pin_shared_rope_half_mla,
-            pin_branches_separate, pin_one_token, pin_uniform, pin_paged_equals_contiguous,
+            pin_shards_sum_to_whole, pin_branches_separate, pin_one_token, pin_uniform, pin_paged_equals_contiguous,
             pin_token_permutation, pin_shift_and_range, pin_empty_sequence, pin_absorb_is_unabsorbed_attention]

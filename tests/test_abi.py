@@ -78,6 +78,37 @@ def test_bad_params_rejected(field, value, code):
     assert L.lib().mlra_last_error().decode()
 
 
+def shard_params(**kw):
+    """One latent head of 128 channels plus RoPE in joint 192-element rows (the shard form)."""
+    base = dict(num_branches=1, d_latent=128, q_stride_b=32 * 192, q_stride_h=192, qr_stride_b=32 * 192,
+                qr_stride_h=192, lat_stride_tok=192, rope_stride_tok=192)
+    base.update(kw)
+    return good_params(**base)
+
+
+def test_shard_form_params():
+    assert rc(shard_params()) == 0
+    assert rc(shard_params(num_heads=1)) == 0
+    assert rc(shard_params(page_size=64, max_pages_per_seq=512)) == 0
+    assert rc(shard_params(dtype=1)) == -3          # bf16 only
+    assert rc(shard_params(num_heads=33)) == -3     # one block of 32 query heads
+    assert rc(shard_params(num_branches=2)) == -3   # 2 x 128 is not a supported latent
+    assert rc(shard_params(q_stride_h=120)) == -2   # below the 128-element latent row
+
+
+def test_shard_workspace_size_with_explicit_splits_needs_no_device():
+    L = _lib()
+    p = shard_params(num_splits=1024)
+    n = ctypes.c_size_t(0)
+    assert L.lib().mlra_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    slots = 1024 + 32
+    expect = (slots * 32 * 128 * 4          # split partials of the output (one latent head)
+              + slots * 1 * 32 * 2 * 4      # running max and sum per partial
+              + (32 + 3) * 8                # tile prefix per sequence, T, G
+              + 1 * 32 * 2 * 32 * 128 * 4)  # projected 64-channel blocks, one group of 32 sequences
+    assert n.value >= expect and n.value % 256 == 0 and n.value < expect + 5 * 256
+
+
 def test_paged_needs_enough_table_columns():
     assert rc(good_params(page_size=64, max_pages_per_seq=511)) == -2
     assert rc(good_params(page_size=64, max_pages_per_seq=512)) == 0

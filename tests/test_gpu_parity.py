@@ -209,8 +209,54 @@ def test_copy_and_read_probes():
     assert int(sink.cpu().numpy().view(np.uint32)[0]) == expect
 
 
+# ----------------------------------------------------------------- the one-latent-head shard form
+SHARD = CONFIGS[7]
+
+
+@pytest.mark.parametrize("page_size", [0, 64])
+@pytest.mark.parametrize("num_splits", [1, 3, 0])
+def test_shard_small_ragged(page_size, num_splits):
+    """One latent head of 128 channels in joint 192-wide rows (one GPU's share of MLRA-4), ragged
+    lengths with NaN in every row no sequence owns; contiguous and paged."""
+    w = SHARD.replace(B=3, lengths=("list", (1, 70, 333)), page_size=page_size)
+    inp = make_inputs(w, seed=17, poison=True, max_seqlen=352)
+    assert_parity(gpu_decode(inp, num_splits), oracle.decode_inputs(inp),
+                  label=f"shard page={page_size}/splits={num_splits}")
+
+
+def test_shard_edge_lengths():
+    w = SHARD.replace(B=len(EDGE_LENGTHS), lengths=("list", EDGE_LENGTHS), joint=False)
+    inp = make_inputs(w, seed=18, poison=True, max_seqlen=192)
+    ref = oracle.decode_inputs(inp)
+    for splits in (0, 5, 64):
+        got = gpu_decode(inp, splits)
+        assert_parity(got, ref, label=f"shard edge splits={splits}")
+        for b, L in enumerate(EDGE_LENGTHS):
+            if L == 0:
+                assert np.all(got[b] == 0.0)
+
+
+def test_four_shards_sum_to_mlra4():
+    """The four latent heads of an MLRA-4 cache decoded apart, each from views of the MLRA-4
+    tensors with its own W_UV block, and summed: the MLRA-4 output (the branch sum done across
+    GPUs in the tensor-parallel layout), against the oracle and against the MLRA-4 kernel."""
+    mlra = _mlra()
+    w = CONFIGS[2].replace(B=4, lengths=("list", (1000, 64, 3000, 777)))
+    inp = make_inputs(w, seed=19)
+    d = inp.to("cuda")
+    total = torch.zeros(4, w.h, 128, dtype=torch.float64, device="cuda")
+    for j in range(4):
+        out = mlra.decode(d.q_nope[:, :, j:j + 1], d.q_rope, d.latent[:, j:j + 1], d.rope, d.seqlens,
+                          d.W_UV[j:j + 1], sm_scale=w.sm_scale, out_scale=w.gamma, max_seqlen=inp.max_seqlen)
+        total += out.double()
+    torch.cuda.synchronize()
+    total = total.cpu().numpy()
+    assert_parity(total, oracle.decode_inputs(inp), label="sum of 4 shards vs oracle")
+    assert_parity(total, gpu_decode(inp), label="sum of 4 shards vs MLRA-4 kernel")
+
+
 # ----------------------------------------------------------------- full-size workloads, sampled sequences
-FULL = {2: (0, 17, 31), 3: (0, 1, 2, 3), 4: (0, 31), 5: (0, 13, 40, 63), 6: (0, 31)}
+FULL = {2: (0, 17, 31), 3: (0, 1, 2, 3), 4: (0, 31), 5: (0, 13, 40, 63), 6: (0, 31), 7: (0, 31)}
 
 
 @pytest.mark.parametrize("cfg", sorted(FULL))
@@ -296,7 +342,7 @@ def test_graph_replay_matches_eager():
 from mlra_workloads import make_absorption_inputs
 
 
-@pytest.mark.parametrize("cfg,shared", [(2, False), (2, True), (4, False), (1, False)])
+@pytest.mark.parametrize("cfg,shared", [(2, False), (2, True), (4, False), (1, False), (7, False)])
 def test_absorb_query_then_decode(cfg, shared):
     """GPU absorption q_nope = W_UK q_pre against the oracle's, then the full three-step decode
     (absorb on the GPU, attend, up-project) against the oracle on the fp64 absorbed query."""

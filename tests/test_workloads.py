@@ -54,9 +54,10 @@ def test_shapes_and_dtypes():
         assert inp.W_UV.shape == (NB, h, DL, 128) and inp.W_UV.dtype == torch.float32
         assert inp.latent.dtype == w.torch_dtype
         if w.joint:
-            assert inp.cache_joint.shape[1] == 576 and inp.q_joint.shape[-1] == 576
+            row = NB * DL + 64  # 576, or 192 for one latent head
+            assert inp.cache_joint.shape[1] == row and inp.q_joint.shape[-1] == row
             assert inp.latent.data_ptr() == inp.cache_joint.data_ptr()
-            assert inp.rope.data_ptr() == inp.cache_joint.data_ptr() + 512 * inp.cache_joint.element_size()
+            assert inp.rope.data_ptr() == inp.cache_joint.data_ptr() + NB * DL * inp.cache_joint.element_size()
 
 
 def test_value_distributions():
