@@ -236,8 +236,9 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {max(args.gpus, world)}); "
-              f"the multi-GPU sharding of the decode is a design note, not a runnable path.", file=sys.stderr)
+        print(f"bench.py: this build runs on one GPU only (asked for {max(args.gpus, world)}). One GPU's share "
+              f"of MLRA-4 split over four GPUs by latent head is --config 7; the cross-GPU sum is not built.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -1,5 +1,7 @@
-"""Seeded synthetic inputs: determinism, shapes, length draws and page-table structure (CPU only)."""
+"""Seeded synthetic inputs: determinism, shapes, length draws and page-table structure; the
+benchmark's one-GPU guard (CPU only)."""
 import math
+import os
 
 import torch
 
@@ -66,3 +68,14 @@ def test_value_distributions():
     assert abs(inp.latent.float().std().item() - 1.0) < 0.02
     assert abs(inp.rope.float().std().item() - math.sqrt(3.0)) < 0.05
     assert abs(inp.W_UV.std().item() - 1.0 / math.sqrt(128)) < 0.002
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark runs on one GPU; asking for more exits with status 2 and says why, before any
+    GPU work (no torch.distributed rendezvous, no device query)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU only" in r.stderr and r.stdout == ""
