@@ -109,7 +109,7 @@ def record_traffic(fetch_csv, write_csv, args):
     """Scale the decode kernel's FETCH_SIZE / WRITE_SIZE (KiB per dispatch) by what the same
     counters read for the copy kernel, whose bytes are known (copy_probe_mib read + written)."""
     import csv
-    from mlra_workloads import CONFIGS, make_inputs
+    from mlra_workloads import WORKLOADS, make_inputs
 
     def means(path):
         acc = {}
@@ -122,7 +122,7 @@ def record_traffic(fetch_csv, write_csv, args):
     copy_bytes = args.copy_probe_mib << 20
     f_scale = copy_bytes / (pick(f, "copy_kernel") * 1024)
     w_scale = copy_bytes / (pick(wr, "copy_kernel") * 1024)
-    w = CONFIGS[args.config]
+    w = WORKLOADS[args.config]
     inp = make_inputs(w, seed=args.config)
     attn = lambda d: next(v for k, v in d.items() if re.search(r"decode_(branch_|hs_|shard_)?kernel", k))
     fetch = attn(f) * 1024 * f_scale
@@ -146,8 +146,8 @@ def gqa_leg(mlra, inp, args, stream, mlra_ms, shard=False):
     shard: one GPU's share of it under four-way tensor parallelism over heads (16 query heads
     over 2 KV heads), to set beside the one-latent-head share of MLRA-4."""
     import torch
-    from mlra_workloads import GQA_CONFIGS, make_gqa_inputs
-    g = GQA_CONFIGS["gqa_bf16_b32_hq64_hkv8_L32k"].replace(B=len(inp.seqlens), lengths=("list", tuple(inp.seqlens.tolist())))
+    from mlra_workloads import GQA_WORKLOADS, make_gqa_inputs
+    g = GQA_WORKLOADS["gqa_bf16_b32_hq64_hkv8_L32k"].replace(B=len(inp.seqlens), lengths=("list", tuple(inp.seqlens.tolist())))
     if shard:
         g = g.replace(Hq=g.Hq // 4, Hkv=g.Hkv // 4)
     gi = make_gqa_inputs(g, seed=args.config, device="cuda")
@@ -236,20 +236,20 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for {max(args.gpus, world)}). One GPU's share "
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}). One GPU's share "
               f"of MLRA-4 split over four GPUs by latent head is --config 7; the cross-GPU sum is not built.",
               file=sys.stderr)
         sys.exit(2)
 
     import torch
     import long_context_decode_mlra_amd as mlra
-    from mlra_workloads import CONFIGS, make_inputs
+    from mlra_workloads import WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
-    w = CONFIGS[args.config]
+    w = WORKLOADS[args.config]
     print(f"bench: generating workload {w.name} (seed {args.config})", file=sys.stderr, flush=True)
     inp = make_inputs(w, seed=args.config)
     d = inp.to(dev)

@@ -25,8 +25,8 @@ from typing import Optional, Sequence
 
 import torch
 
-__all__ = ["Workload", "CONFIGS", "make_inputs", "DecodeInputs", "draw_lengths", "make_absorption_inputs",
-           "GqaWorkload", "GQA_CONFIGS", "GqaInputs", "make_gqa_inputs"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "DecodeInputs", "draw_lengths", "make_absorption_inputs",
+           "GqaWorkload", "GQA_WORKLOADS", "GqaInputs", "make_gqa_inputs"]
 
 D_ROPE = 64
 D_V = 128
@@ -78,7 +78,7 @@ class Workload:
 
 
 # The workloads of the decode benchmark. Seed = workload number.
-CONFIGS = {
+WORKLOADS = {
     1: Workload("mlra4_f32_b1_h16_L1k", "f32", B=1, h=16, NB=4, DL=128, lengths=("fixed", 1024)),
     2: Workload("mlra4_bf16_b32_h32_L32k", "bf16", B=32, h=32, NB=4, DL=128, lengths=("fixed", 32768),
                 rope_std=math.sqrt(1536.0 / 512.0)),
@@ -325,7 +325,7 @@ class GqaWorkload:
         return dataclasses.replace(self, **kw)
 
 
-GQA_CONFIGS = {
+GQA_WORKLOADS = {
     "gqa_bf16_b32_hq64_hkv8_L32k": GqaWorkload("gqa_bf16_b32_hq64_hkv8_L32k", B=32, Hq=64, Hkv=8,
                                                lengths=("fixed", 32768)),
 }

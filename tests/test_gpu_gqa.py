@@ -8,12 +8,12 @@ import pytest
 import torch
 
 import oracle
-from mlra_workloads import GQA_CONFIGS, GqaInputs, make_gqa_inputs
+from mlra_workloads import GQA_WORKLOADS, GqaInputs, make_gqa_inputs
 
 pytestmark = pytest.mark.gpu
 
 MAX_ABS, REL_L2 = 2e-2, 5e-3
-W64 = GQA_CONFIGS["gqa_bf16_b32_hq64_hkv8_L32k"]
+W64 = GQA_WORKLOADS["gqa_bf16_b32_hq64_hkv8_L32k"]
 
 
 def _mlra():

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from mlra_workloads import CONFIGS, make_inputs
+from mlra_workloads import WORKLOADS, make_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -51,11 +51,11 @@ def assert_parity(got, ref, max_abs=MAX_ABS, rel_l2=REL_L2, label=""):
 
 
 SMALL = {
-    "mlra4_bf16": CONFIGS[2],
-    "mla_bf16": CONFIGS[4],
-    "mlra2_bf16": CONFIGS[2].replace(name="mlra2", NB=2, DL=256, rope_std=1.0),
-    "mlra4_f32": CONFIGS[1].replace(h=32),
-    "mla_f32": CONFIGS[4].replace(dtype="f32"),
+    "mlra4_bf16": WORKLOADS[2],
+    "mla_bf16": WORKLOADS[4],
+    "mlra2_bf16": WORKLOADS[2].replace(name="mlra2", NB=2, DL=256, rope_std=1.0),
+    "mlra4_f32": WORKLOADS[1].replace(h=32),
+    "mla_f32": WORKLOADS[4].replace(dtype="f32"),
 }
 
 
@@ -87,7 +87,7 @@ def test_mlra4_joint_rows(cfg):
     """MLRA-4 with queries and cache stored as joint rows ([.., 576]: the four latent heads, then
     RoPE), so every query and cache stride differs from the separate-tensor layout: contiguous and
     paged bf16 (one wave per branch) and fp32 (whole tiles)."""
-    w = CONFIGS[cfg].replace(B=4, lengths=("list", (1, 70, 333, 64)), joint=True)
+    w = WORKLOADS[cfg].replace(B=4, lengths=("list", (1, 70, 333, 64)), joint=True)
     inp = make_inputs(w, seed=13, poison=True)
     tol = dict(rel_l2=1e-4, max_abs=1e-3) if w.dtype == "f32" else {}
     ref = oracle.decode_inputs(inp)
@@ -100,7 +100,7 @@ EDGE_LENGTHS = (0, 1, 2, 31, 32, 33, 63, 64, 65, 95, 96, 97, 0, 128, 129, 5)
 
 @pytest.mark.parametrize("paged", [False, True])
 def test_edge_lengths_and_poisoned_padding(paged):
-    w = CONFIGS[5 if paged else 3].replace(B=len(EDGE_LENGTHS), lengths=("list", EDGE_LENGTHS))
+    w = WORKLOADS[5 if paged else 3].replace(B=len(EDGE_LENGTHS), lengths=("list", EDGE_LENGTHS))
     inp = make_inputs(w, seed=11, poison=True, max_seqlen=192)
     for splits in (0, 5, 64):
         got = gpu_decode(inp, splits)
@@ -115,17 +115,17 @@ def test_edge_lengths_and_poisoned_padding(paged):
 def test_head_counts(h):
     """Head counts below, between and at the 32-head blocks (1 and 5 leave most MFMA columns
     empty; 33 puts one head in a second block)."""
-    w = CONFIGS[2].replace(B=2, h=h, lengths=("list", (200, 45)))
+    w = WORKLOADS[2].replace(B=2, h=h, lengths=("list", (200, 45)))
     inp = make_inputs(w, seed=h)
     assert_parity(gpu_decode(inp), oracle.decode_inputs(inp), label=f"h={h}")
-    wm = CONFIGS[4].replace(B=2, h=h, lengths=("list", (90, 260)))
+    wm = WORKLOADS[4].replace(B=2, h=h, lengths=("list", (90, 260)))
     inp = make_inputs(wm, seed=h + 1)
     assert_parity(gpu_decode(inp), oracle.decode_inputs(inp), label=f"mla h={h}")
 
 
 def test_cfg1_full_f32():
     """fp32 everywhere, B=1, h=16, L=1024 (the whole workload)."""
-    inp = make_inputs(CONFIGS[1], seed=1)
+    inp = make_inputs(WORKLOADS[1], seed=1)
     got = gpu_decode(inp)
     ref = oracle.decode_inputs(inp)
     assert_parity(got, ref, label="cfg1", rel_l2=1e-4, max_abs=1e-3)
@@ -133,7 +133,7 @@ def test_cfg1_full_f32():
 
 def test_large_logits_stay_finite():
     """Logits of several hundred: the online softmax must not overflow."""
-    w = CONFIGS[2].replace(B=2, lengths=("list", (300, 64)), sm_scale=1.0)
+    w = WORKLOADS[2].replace(B=2, lengths=("list", (300, 64)), sm_scale=1.0)
     inp = make_inputs(w, seed=3)
     inp.q_rope.mul_(4)
     got = gpu_decode(inp)
@@ -143,7 +143,7 @@ def test_large_logits_stay_finite():
 
 
 def test_deterministic_bitwise():
-    w = CONFIGS[5].replace(B=5, lengths=("list", (1000, 64, 3000, 1, 777)))
+    w = WORKLOADS[5].replace(B=5, lengths=("list", (1000, 64, 3000, 1, 777)))
     inp = make_inputs(w, seed=5)
     a = gpu_decode(inp)
     b = gpu_decode(inp)
@@ -151,7 +151,7 @@ def test_deterministic_bitwise():
 
 
 def test_split_counts_agree():
-    w = CONFIGS[2].replace(B=4, lengths=("list", (2000, 31, 4096, 700)))
+    w = WORKLOADS[2].replace(B=4, lengths=("list", (2000, 31, 4096, 700)))
     inp = make_inputs(w, seed=9)
     ref = oracle.decode_inputs(inp)
     outs = []
@@ -210,7 +210,7 @@ def test_copy_and_read_probes():
 
 
 # ----------------------------------------------------------------- the one-latent-head shard form
-SHARD = CONFIGS[7]
+SHARD = WORKLOADS[7]
 
 
 @pytest.mark.parametrize("page_size", [0, 64])
@@ -241,7 +241,7 @@ def test_four_shards_sum_to_mlra4():
     tensors with its own W_UV block, and summed: the MLRA-4 output (the branch sum done across
     GPUs in the tensor-parallel layout), against the oracle and against the MLRA-4 kernel."""
     mlra = _mlra()
-    w = CONFIGS[2].replace(B=4, lengths=("list", (1000, 64, 3000, 777)))
+    w = WORKLOADS[2].replace(B=4, lengths=("list", (1000, 64, 3000, 777)))
     inp = make_inputs(w, seed=19)
     d = inp.to("cuda")
     total = torch.zeros(4, w.h, 128, dtype=torch.float64, device="cuda")
@@ -263,7 +263,7 @@ FULL = {2: (0, 17, 31), 3: (0, 1, 2, 3), 4: (0, 31), 5: (0, 13, 40, 63), 6: (0, 
 def test_full_size_sampled(cfg):
     """The workload at its full size in the launch configuration the benchmark times
     (num_splits = one per resident slot); the oracle checks sampled sequences."""
-    w = CONFIGS[cfg]
+    w = WORKLOADS[cfg]
     inp = make_inputs(w, seed=cfg)
     print(f"cfg{cfg}: B={w.B} tokens={inp.total_tokens} max_seqlen={inp.max_seqlen}", flush=True)
     got = gpu_decode(inp, 0)
@@ -279,7 +279,7 @@ def test_two_sequence_groups_and_workspace_reuse():
     mlra = _mlra()
     rng = np.random.default_rng(40)
     Ls = tuple(int(x) for x in rng.integers(0, 900, size=40))
-    w = CONFIGS[2].replace(B=40, lengths=("list", Ls))
+    w = WORKLOADS[2].replace(B=40, lengths=("list", Ls))
     inp = make_inputs(w, seed=40, poison=True)
     d = inp.to("cuda")
     dec = mlra.Decoder(d.q_nope, d.q_rope, d.latent, d.rope, seqlens=d.seqlens, W_UV=d.W_UV, sm_scale=w.sm_scale,
@@ -296,7 +296,7 @@ def test_two_sequence_groups_and_workspace_reuse():
 def test_one_sequence_of_a_million_tokens():
     """Maximum length on one GPU-resident sequence: B=1, L=2^20 (1.2 GB of cache). Every split
     of the default launch falls in the same sequence, so the combine merges 512+1 slots for it."""
-    w = CONFIGS[2].replace(B=1, lengths=("list", (1 << 20,)))
+    w = WORKLOADS[2].replace(B=1, lengths=("list", (1 << 20,)))
     inp = make_inputs(w, seed=41)
     print(f"B=1 L={1 << 20}", flush=True)
     got = gpu_decode(inp, 0)
@@ -308,7 +308,7 @@ def test_a_thousand_short_sequences():
     one or two tiles that span several sequences), paged and contiguous."""
     rng = np.random.default_rng(42)
     Ls = tuple(int(x) for x in rng.integers(0, 101, size=1000))
-    for w in (CONFIGS[2].replace(B=1000, lengths=("list", Ls)), CONFIGS[5].replace(B=1000, lengths=("list", Ls))):
+    for w in (WORKLOADS[2].replace(B=1000, lengths=("list", Ls)), WORKLOADS[5].replace(B=1000, lengths=("list", Ls))):
         inp = make_inputs(w, seed=42, poison=True)
         got = gpu_decode(inp, 0)
         assert np.all(got[[b for b, L in enumerate(Ls) if L == 0]] == 0)
@@ -319,7 +319,7 @@ def test_graph_replay_matches_eager():
     """A captured decode step replayed several times, with eager work in between, gives the
     eager result every time (the step records kernel launches only)."""
     mlra = _mlra()
-    w = CONFIGS[5].replace(B=6, lengths=("list", (700, 1, 2048, 65, 0, 333)))
+    w = WORKLOADS[5].replace(B=6, lengths=("list", (700, 1, 2048, 65, 0, 333)))
     inp = make_inputs(w, seed=12)
     d = inp.to("cuda")
     dec = mlra.Decoder(d.q_nope, d.q_rope, d.latent, d.rope, seqlens=d.seqlens, W_UV=d.W_UV, sm_scale=w.sm_scale,
@@ -347,7 +347,7 @@ def test_absorb_query_then_decode(cfg, shared):
     """GPU absorption q_nope = W_UK q_pre against the oracle's, then the full three-step decode
     (absorb on the GPU, attend, up-project) against the oracle on the fp64 absorbed query."""
     mlra = _mlra()
-    w = CONFIGS[cfg].replace(B=3, lengths=("list", (257, 1, 90)))
+    w = WORKLOADS[cfg].replace(B=3, lengths=("list", (257, 1, 90)))
     inp = make_inputs(w, seed=cfg, max_seqlen=288)
     q_pre, W_UK = make_absorption_inputs(w, seed=cfg, B=3, shared_query=shared)
     d = inp.to("cuda")

@@ -5,7 +5,7 @@ import pytest
 import gqa_pins
 import oracle
 from oracle import gqa_oracle as G
-from mlra_workloads import GQA_CONFIGS, make_gqa_inputs
+from mlra_workloads import GQA_WORKLOADS, make_gqa_inputs
 
 
 @pytest.mark.parametrize("pin", gqa_pins.ALL_PINS, ids=lambda f: f.__name__)
@@ -81,7 +81,7 @@ def test_unmutated_oracle_passes_every_pin():
 
 
 def test_generated_workload_shapes_and_oracle_run():
-    w = GQA_CONFIGS["gqa_bf16_b32_hq64_hkv8_L32k"].replace(B=2, lengths=("list", (33, 0)), page_size=32)
+    w = GQA_WORKLOADS["gqa_bf16_b32_hq64_hkv8_L32k"].replace(B=2, lengths=("list", (33, 0)), page_size=32)
     inp = make_gqa_inputs(w, seed=3, poison=True)
     assert inp.q.shape == (2, 64, 128) and inp.k_cache.shape[1:] == (8, 128)
     out = oracle.gqa_decode_inputs(inp)

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import oracle_pins
-from mlra_workloads import CONFIGS, make_inputs
+from mlra_workloads import WORKLOADS, make_inputs
 
 
 @pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda f: f.__name__)
@@ -27,7 +27,7 @@ def test_split_kv_equals_single_pass(chunk):
 
 
 def test_split_kv_real_widths_bf16_inputs():
-    w = CONFIGS[2].replace(B=2, lengths=("list", (300, 65)))
+    w = WORKLOADS[2].replace(B=2, lengths=("list", (300, 65)))
     inp = make_inputs(w, seed=2)
     a = oracle.decode_inputs(inp)
     s = oracle.decode_split(inp.q_nope, inp.q_rope, inp.latent, inp.rope, inp.W_UV, inp.seqlens,
@@ -38,7 +38,7 @@ def test_split_kv_real_widths_bf16_inputs():
 def test_poisoned_rows_are_never_read():
     """NaN in every row no sequence owns (padding, unused page tails) must not reach the output."""
     for k in (3, 5):
-        w = CONFIGS[k].replace(B=3, lengths=("list", (70, 1, 129)))
+        w = WORKLOADS[k].replace(B=3, lengths=("list", (70, 1, 129)))
         inp = make_inputs(w, seed=k, poison=True, max_seqlen=160)
         out = oracle.decode_inputs(inp)
         assert np.all(np.isfinite(out))
@@ -48,6 +48,6 @@ def test_per_token_bytes():
     """Both cache layouts hold 576 elements per token: 4 x 128 + 64 (MLRA-4) and 512 + 64 (MLA),
     i.e. 4.5 d_h with d_h = 128; one MLRA branch's logit space is 128 + 64 = 1.5 d_h."""
     for k in (1, 2, 3, 4, 5):
-        assert CONFIGS[k].token_elems == 576 == 4.5 * 128
-    assert CONFIGS[2].DL + CONFIGS[2].DR == 192 == 1.5 * 128
-    assert math.isclose(CONFIGS[2].gamma, 0.5) and math.isclose(CONFIGS[4].gamma, 1.0)
+        assert WORKLOADS[k].token_elems == 576 == 4.5 * 128
+    assert WORKLOADS[2].DL + WORKLOADS[2].DR == 192 == 1.5 * 128
+    assert math.isclose(WORKLOADS[2].gamma, 0.5) and math.isclose(WORKLOADS[4].gamma, 1.0)

@@ -5,11 +5,11 @@ import os
 
 import torch
 
-from mlra_workloads import CONFIGS, make_inputs
+from mlra_workloads import WORKLOADS, make_inputs
 
 
 def test_same_seed_same_bytes():
-    w = CONFIGS[5].replace(B=6, lengths=("loguniform", 10, 300))
+    w = WORKLOADS[5].replace(B=6, lengths=("loguniform", 10, 300))
     a, b = make_inputs(w, seed=5), make_inputs(w, seed=5)
     def raw(t):
         return t.contiguous().view(-1).view(torch.uint8) if t.dtype.is_floating_point else t
@@ -22,10 +22,10 @@ def test_same_seed_same_bytes():
 def test_length_draws_in_range():
     from mlra_workloads import draw_lengths
     gen = torch.Generator().manual_seed(3)
-    Ls = draw_lengths(CONFIGS[3], gen)
+    Ls = draw_lengths(WORKLOADS[3], gen)
     assert len(Ls) == 4 and all(65536 <= L <= 131072 for L in Ls)
     gen = torch.Generator().manual_seed(5)
-    Ls = draw_lengths(CONFIGS[5], gen)
+    Ls = draw_lengths(WORKLOADS[5], gen)
     assert len(Ls) == 64 and all(1024 <= L <= 65536 for L in Ls)
     # log-uniform: the median sits near the geometric mean sqrt(1024 * 65536) = 8192
     med = sorted(Ls)[32]
@@ -33,7 +33,7 @@ def test_length_draws_in_range():
 
 
 def test_page_table_is_a_permutation_of_the_pool():
-    w = CONFIGS[5].replace(B=7, lengths=("list", (1, 64, 65, 0, 200, 128, 3)))
+    w = WORKLOADS[5].replace(B=7, lengths=("list", (1, 64, 65, 0, 200, 128, 3)))
     inp = make_inputs(w, seed=5)
     P = w.page_size
     used = []
@@ -47,7 +47,7 @@ def test_page_table_is_a_permutation_of_the_pool():
 
 
 def test_shapes_and_dtypes():
-    for k, w in CONFIGS.items():
+    for k, w in WORKLOADS.items():
         w = w.replace(B=2, lengths=("list", (33, 5)))
         inp = make_inputs(w, seed=k)
         B, h, NB, DL = 2, w.h, w.NB, w.DL
@@ -63,7 +63,7 @@ def test_shapes_and_dtypes():
 
 
 def test_value_distributions():
-    w = CONFIGS[2].replace(B=2, lengths=("fixed", 4096))
+    w = WORKLOADS[2].replace(B=2, lengths=("fixed", 4096))
     inp = make_inputs(w, seed=2)
     assert abs(inp.latent.float().std().item() - 1.0) < 0.02
     assert abs(inp.rope.float().std().item() - math.sqrt(3.0)) < 0.05
