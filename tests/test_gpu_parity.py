@@ -236,6 +236,12 @@ def test_shard_edge_lengths():
                 assert np.all(got[b] == 0.0)
 
 
+def test_shard_deterministic_bitwise():
+    w = SHARD.replace(B=5, lengths=("list", (1000, 64, 3000, 1, 777)))
+    inp = make_inputs(w, seed=20)
+    assert np.array_equal(gpu_decode(inp), gpu_decode(inp))
+
+
 def test_four_shards_sum_to_mlra4():
     """The four latent heads of an MLRA-4 cache decoded apart, each from views of the MLRA-4
     tensors with its own W_UV block, and summed: the MLRA-4 output (the branch sum done across
@@ -305,14 +311,15 @@ def test_one_sequence_of_a_million_tokens():
 
 def test_a_thousand_short_sequences():
     """B=1000 ragged sequences of 0..100 tokens (32 sequence groups in the combine; splits of
-    one or two tiles that span several sequences), paged and contiguous."""
+    one or two tiles that span several sequences), paged and contiguous; and the shard form, paged."""
     rng = np.random.default_rng(42)
     Ls = tuple(int(x) for x in rng.integers(0, 101, size=1000))
-    for w in (WORKLOADS[2].replace(B=1000, lengths=("list", Ls)), WORKLOADS[5].replace(B=1000, lengths=("list", Ls))):
+    for w in (WORKLOADS[2].replace(B=1000, lengths=("list", Ls)), WORKLOADS[5].replace(B=1000, lengths=("list", Ls)),
+              WORKLOADS[7].replace(B=1000, lengths=("list", Ls), page_size=64)):
         inp = make_inputs(w, seed=42, poison=True)
         got = gpu_decode(inp, 0)
         assert np.all(got[[b for b, L in enumerate(Ls) if L == 0]] == 0)
-        assert_parity(got, oracle.decode_inputs(inp), label=f"B=1000 page={w.page_size}")
+        assert_parity(got, oracle.decode_inputs(inp), label=f"B=1000 {w.name} page={w.page_size}")
 
 
 def test_graph_replay_matches_eager():
