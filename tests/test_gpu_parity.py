@@ -345,6 +345,34 @@ def test_graph_replay_matches_eager():
     assert_parity(eager.cpu().double().numpy(), oracle.decode_inputs(inp), label="graph")
 
 
+def test_two_streams_two_workspaces():
+    """Two decodes with their own workspaces, enqueued on two streams (default priority) so that
+    they may run at the same time, give the bits each gives alone."""
+    mlra = _mlra()
+    decs, alone = [], []
+    for k, w in enumerate((WORKLOADS[2].replace(B=3, lengths=("list", (2000, 31, 900))),
+                           WORKLOADS[5].replace(B=4, lengths=("list", (700, 1, 1500, 64))))):
+        inp = make_inputs(w, seed=50 + k)
+        d = inp.to("cuda")
+        dec = mlra.Decoder(d.q_nope, d.q_rope, d.latent, d.rope, seqlens=d.seqlens, W_UV=d.W_UV, sm_scale=w.sm_scale,
+                           out_scale=w.gamma, max_seqlen=inp.max_seqlen, block_table=d.block_table,
+                           page_size=w.page_size)
+        alone.append(dec().clone())
+        decs.append((dec, d))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for (dec, _), st in zip(decs, streams):
+            dec.out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        for (dec, _), st in zip(decs, streams):
+            with torch.cuda.stream(st):
+                dec(st)
+        torch.cuda.synchronize()
+        for (dec, _), ref in zip(decs, alone):
+            assert torch.equal(dec.out, ref), f"rep {rep}"
+
+
 # ----------------------------------------------------------------- query-side absorption (decode step 1)
 from mlra_workloads import make_absorption_inputs
 
