@@ -111,17 +111,18 @@ __global__ __launch_bounds__(64) void gqa_decode_kernel(GqaArgs a) {
   const bool head_ok = n16 < a.group;
   const int head = kh * a.group + n16;
 
-  const Plan plan = make_plan(a.seqlens, a.B, a.G_req);
-  if (gs == 0 && kh == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
+  const Lens lens = load_lens(a.seqlens, a.B);
+  const Plan plan = make_plan(lens, a.G_req);
+  if (gs == 0 && kh == 0) write_prefix(lens, plan, a.prefix);
   if (gs >= plan.G) return;
-  SegmentWalk walk = begin_walk(a.seqlens, a.B, gs, plan);
+  SegmentWalk walk = begin_walk(lens, gs, plan);
 
-  int b, ta, te;
-  while (next_segment(a.seqlens, a.B, walk, b, ta, te)) {
+  int b, ta, te, L;
+  while (next_segment(lens, walk, b, ta, te, L)) {
     b = __builtin_amdgcn_readfirstlane(b);
     ta = __builtin_amdgcn_readfirstlane(ta);
     te = __builtin_amdgcn_readfirstlane(te);
-    const int L = scalar_read(a.seqlens + b);
+    L = __builtin_amdgcn_readfirstlane(L);
 
     // Query operand of K step st: channels 32*st + 8*g4 .. +8 of this lane's head.
     bf16x8 qv[4];

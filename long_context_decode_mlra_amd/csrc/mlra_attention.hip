@@ -110,8 +110,8 @@ struct DecodeArgs {
 // The split plan of a launch of G_req workgroups, switched to G_small splits when the tiles
 // would give fewer than kMinTilesPerSplit per split. Workgroups g >= G exit at once; the first
 // G_small of them land one per compute unit (workgroups are dealt round-robin over the XCDs).
-__device__ __forceinline__ Plan split_plan(const DecodeArgs& a) {
-  Plan p = make_plan(a.seqlens, a.B, a.G_req);
+__device__ __forceinline__ Plan split_plan(const DecodeArgs& a, const Lens& lens) {
+  Plan p = make_plan(lens, a.G_req);
   if (a.G_small > 0 && p.T < int64_t(kMinTilesPerSplit) * a.G_req) p.G = int(p.T < a.G_small ? p.T : a.G_small);
   return p;
 }
@@ -418,19 +418,20 @@ void decode_kernel(DecodeArgs a) {
   const int head = hb * kHeadBlock + n;
   const bool head_ok = head < a.h;
 
-  const Plan plan = split_plan(a);
-  if (blockIdx.x == 0 && wave == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
+  const Lens lens = load_lens(a.seqlens, a.B);
+  const Plan plan = split_plan(a, lens);
+  if (blockIdx.x == 0 && wave == 0) write_prefix(lens, plan, a.prefix);
   if (int(blockIdx.x) >= plan.G) return;
   const int g = xcd_major_split(blockIdx.x, plan.G);
-  SegmentWalk walk = begin_walk(a.seqlens, a.B, g, plan);
+  SegmentWalk walk = begin_walk(lens, g, plan);
 
-  int b, ta, te;
-  while (next_segment(a.seqlens, a.B, walk, b, ta, te)) {
+  int b, ta, te, L;
+  while (next_segment(lens, walk, b, ta, te, L)) {
     // Segment bounds are the same in every lane: keep them (and the loop) scalar.
     b = __builtin_amdgcn_readfirstlane(b);
     ta = __builtin_amdgcn_readfirstlane(ta);
     te = __builtin_amdgcn_readfirstlane(te);
-    const int L = scalar_read(a.seqlens + b);
+    L = __builtin_amdgcn_readfirstlane(L);
     QOps<T, NB> q;
     floatx16 O[4] = {};
     float m_run = -INFINITY;
@@ -658,12 +659,11 @@ struct BrAcc {
 };
 
 // Tiles [ta, te) of sequence b for latent head j, from the queries to the softmax state.
-__device__ __forceinline__ void br_segment(const DecodeArgs& a, int b, int ta, int te, int j, int lane,
+__device__ __forceinline__ void br_segment(const DecodeArgs& a, int b, int L, int ta, int te, int j, int lane,
                                            bool head_ok, unsigned char* ring, const uint32_t (&full)[kBrLoads],
                                            BrAcc& acc) {
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int L = scalar_read(a.seqlens + b);
   // Query operands: latent K step ks covers channels 16*ks + 8*hh .. +8 of latent head j,
   // RoPE K step rs channels 16*rs + 8*hh .. +8. Lanes past h load head 0 and are zeroed.
   bf16x8 ql[8], qr[4];
@@ -823,32 +823,33 @@ __device__ __forceinline__ void br_store_partial(const DecodeArgs& a, int64_t ps
 // both are stored with no loads in flight. The first segment runs in its own copy of the tile
 // loop, free of the held registers.
 template <int NB>
-__device__ __forceinline__ void br_run_split(const DecodeArgs& a, const Plan& plan, int g, int j, int lane,
-                                             bool head_ok, unsigned char* ring, const uint32_t (&full)[kBrLoads]) {
+__device__ __forceinline__ void br_run_split(const DecodeArgs& a, const Lens& lens, const Plan& plan, int g, int j,
+                                             int lane, bool head_ok, unsigned char* ring,
+                                             const uint32_t (&full)[kBrLoads]) {
   const int n = lane & 31;
   const int hh = lane >> 5;
-  SegmentWalk walk = begin_walk(a.seqlens, a.B, g, plan);
-  int b, ta, te;
-  if (!next_segment(a.seqlens, a.B, walk, b, ta, te)) return;
+  SegmentWalk walk = begin_walk(lens, g, plan);
+  int b, ta, te, L;
+  if (!next_segment(lens, walk, b, ta, te, L)) return;
   b = __builtin_amdgcn_readfirstlane(b);
   BrAcc first;
-  br_segment(a, b, __builtin_amdgcn_readfirstlane(ta), __builtin_amdgcn_readfirstlane(te), j, lane, head_ok, ring,
-             full, first);
+  br_segment(a, b, __builtin_amdgcn_readfirstlane(L), __builtin_amdgcn_readfirstlane(ta),
+             __builtin_amdgcn_readfirstlane(te), j, lane, head_ok, ring, full, first);
   const int64_t slot0 = int64_t(g) + b;
   const float l0 = halves_sum(first.l);
   if (walk.cur >= walk.end) {
     if (head_ok) br_store_partial<NB>(a, slot0, j, n, hh, first, l0);
     return;
   }
-  while (next_segment(a.seqlens, a.B, walk, b, ta, te)) {
+  while (next_segment(lens, walk, b, ta, te, L)) {
     // LDS reads returned before this segment's loads reuse the ring (a builtin: the
     // compiler's own wait tracking then starts the segment clean).
     __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
     asm volatile("" ::: "memory");
     b = __builtin_amdgcn_readfirstlane(b);
     BrAcc cur;
-    br_segment(a, b, __builtin_amdgcn_readfirstlane(ta), __builtin_amdgcn_readfirstlane(te), j, lane, head_ok, ring,
-               full, cur);
+    br_segment(a, b, __builtin_amdgcn_readfirstlane(L), __builtin_amdgcn_readfirstlane(ta),
+               __builtin_amdgcn_readfirstlane(te), j, lane, head_ok, ring, full, cur);
     const float l_tot = halves_sum(cur.l);
     const bool last = walk.cur >= walk.end;
     if (head_ok) {
@@ -875,10 +876,11 @@ void decode_branch_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < kBrLoads; ++i) full[i] = br_load_offset(a, i, j, lane, kTile - 1);
 
-  const Plan plan = split_plan(a);
-  if (blockIdx.x == 0 && j == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
+  const Lens lens = load_lens(a.seqlens, a.B);
+  const Plan plan = split_plan(a, lens);
+  if (blockIdx.x == 0 && j == 0) write_prefix(lens, plan, a.prefix);
   if (int(blockIdx.x) >= plan.G) return;
-  br_run_split<4>(a, plan, xcd_major_split(blockIdx.x, plan.G), j, lane, head_ok, ring, full);
+  br_run_split<4>(a, lens, plan, xcd_major_split(blockIdx.x, plan.G), j, lane, head_ok, ring, full);
 }
 
 // ------------------------------------------------------------------ one latent head (shard form)
@@ -899,13 +901,14 @@ void decode_shard_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < kBrLoads; ++i) full[i] = br_load_offset(a, i, 0, lane, kTile - 1);
 
-  const Plan plan = split_plan(a);
-  if (blockIdx.x == 0 && wave == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
+  const Lens lens = load_lens(a.seqlens, a.B);
+  const Plan plan = split_plan(a, lens);
+  if (blockIdx.x == 0 && wave == 0) write_prefix(lens, plan, a.prefix);
   const int wgs = (plan.G + 3) / 4;  // workgroups holding at least one split
   if (int(blockIdx.x) >= wgs) return;
   const int g = 4 * xcd_major_split(blockIdx.x, wgs) + wave;
   if (g >= plan.G) return;
-  br_run_split<1>(a, plan, g, 0, lane, head_ok, ring, full);
+  br_run_split<1>(a, lens, plan, g, 0, lane, head_ok, ring, full);
 }
 
 // ------------------------------------------------------------------ split-head decode (NB = 1, 2; bf16)
@@ -946,18 +949,19 @@ void decode_hs_kernel(DecodeArgs a) {
   const int head = 16 * hq + n16;
   const bool head_ok = head < a.h;
 
-  const Plan plan = split_plan(a);
-  if (blockIdx.x == 0 && wave == 0) write_prefix(a.seqlens, a.B, plan, a.prefix);
+  const Lens lens = load_lens(a.seqlens, a.B);
+  const Plan plan = split_plan(a, lens);
+  if (blockIdx.x == 0 && wave == 0) write_prefix(lens, plan, a.prefix);
   if (int(blockIdx.x) >= plan.G) return;
   const int gsplit = xcd_major_split(blockIdx.x, plan.G);
-  SegmentWalk walk = begin_walk(a.seqlens, a.B, gsplit, plan);
+  SegmentWalk walk = begin_walk(lens, gsplit, plan);
 
-  int b, ta, te;
-  while (next_segment(a.seqlens, a.B, walk, b, ta, te)) {
+  int b, ta, te, L;
+  while (next_segment(lens, walk, b, ta, te, L)) {
     b = __builtin_amdgcn_readfirstlane(b);
     ta = __builtin_amdgcn_readfirstlane(ta);
     te = __builtin_amdgcn_readfirstlane(te);
-    const int L = scalar_read(a.seqlens + b);
+    L = __builtin_amdgcn_readfirstlane(L);
 
     // The first tile is on its way while the queries load.
     issue_tile_dma<__bf16, NB, HB>(a, b, L, ta, wave, lane, smem);

@@ -51,13 +51,41 @@ __device__ __forceinline__ int64_t wave_sum(int64_t v) {
   return v;
 }
 
-// Every lane of the calling wave gets the same plan.
-__device__ inline Plan make_plan(const int32_t* __restrict__ seqlens, int B, int G_req) {
+// The batch's sequence lengths, read from memory once per wave: lane l holds seqlens[l] for
+// l < min(B, 64), so the plan and the walk of a batch of up to 64 sequences cost one load
+// instead of a chain of dependent ones. Lengths past the first 64 are read when asked for.
+struct Lens {
+  const int32_t* p;
+  int B;
+  int32_t reg;
+};
+
+__device__ __forceinline__ Lens load_lens(const int32_t* __restrict__ p, int B) {
   const int lane = threadIdx.x & 63;
-  int64_t s = 0;
-  for (int b = lane; b < B; b += 64) s += tiles_of(seqlens[b]);
+  Lens s;
+  s.p = p;
+  s.B = B;
+  s.reg = lane < B ? p[lane] : 0;
+  return s;
+}
+
+// Length of sequence base + lane in every lane (0 past B); base is a multiple of 64.
+__device__ __forceinline__ int lane_len(const Lens& s, int base) {
+  const int b = base + (threadIdx.x & 63);
+  return base == 0 ? s.reg : (b < s.B ? s.p[b] : 0);
+}
+
+// Length of sequence b, 0 <= b < B, the same b in every lane.
+__device__ __forceinline__ int len_of(const Lens& s, int b) {
+  return b < 64 ? __builtin_amdgcn_readlane(s.reg, b) : scalar_read(s.p + b);
+}
+
+// Every lane of the calling wave gets the same plan.
+__device__ inline Plan make_plan(const Lens& s, int G_req) {
+  int64_t t = 0;
+  for (int base = 0; base < s.B; base += 64) t += tiles_of(lane_len(s, base));
   Plan p;
-  p.T = wave_sum(s);
+  p.T = wave_sum(t);
   p.G = int(p.T < G_req ? p.T : G_req);
   return p;
 }
@@ -81,16 +109,15 @@ __device__ __forceinline__ int64_t wave_inclusive_scan(int64_t v) {
 }
 
 // The sequence b holding global tile x (< T) and its first global tile P_b.
-__device__ inline void find_sequence(const int32_t* __restrict__ seqlens, int B, int64_t x, int& b_out,
-                              int64_t& P_out) {
+__device__ inline void find_sequence(const Lens& s, int64_t x, int& b_out, int64_t& P_out) {
   const int lane = threadIdx.x & 63;
   int64_t carry = 0;
-  for (int base = 0; base < B; base += 64) {
+  for (int base = 0; base < s.B; base += 64) {
     const int b = base + lane;
-    const int64_t t = b < B ? tiles_of(seqlens[b]) : 0;
+    const int64_t t = tiles_of(lane_len(s, base));
     const int64_t incl = wave_inclusive_scan(t);
     const int64_t excl = carry + incl - t;
-    const unsigned long long hit = __ballot(b < B && t > 0 && excl <= x && x < excl + t);
+    const unsigned long long hit = __ballot(b < s.B && t > 0 && excl <= x && x < excl + t);
     if (hit) {
       const int src = __ffsll(hit) - 1;
       b_out = base + src;
@@ -99,26 +126,26 @@ __device__ inline void find_sequence(const int32_t* __restrict__ seqlens, int B,
     }
     carry += __shfl(incl, 63, 64);
   }
-  b_out = B;
+  b_out = s.B;
   P_out = carry;
 }
 
 // prefix[b] = first global tile of sequence b (b <= B), prefix[B+1] = T, prefix[B+2] = G.
 // Called by one whole wave.
-__device__ inline void write_prefix(const int32_t* __restrict__ seqlens, int B, const Plan& p, int64_t* prefix) {
+__device__ inline void write_prefix(const Lens& s, const Plan& p, int64_t* prefix) {
   const int lane = threadIdx.x & 63;
   int64_t carry = 0;
-  for (int base = 0; base < B; base += 64) {
+  for (int base = 0; base < s.B; base += 64) {
     const int b = base + lane;
-    const int64_t t = b < B ? tiles_of(seqlens[b]) : 0;
+    const int64_t t = tiles_of(lane_len(s, base));
     const int64_t incl = wave_inclusive_scan(t);
-    if (b < B) prefix[b] = carry + incl - t;
+    if (b < s.B) prefix[b] = carry + incl - t;
     carry += __shfl(incl, 63, 64);
   }
   if (lane == 0) {
-    prefix[B] = carry;
-    prefix[B + 1] = p.T;
-    prefix[B + 2] = p.G;
+    prefix[s.B] = carry;
+    prefix[s.B + 1] = p.T;
+    prefix[s.B + 2] = p.G;
   }
 }
 
@@ -129,24 +156,26 @@ struct SegmentWalk {
   int64_t end; // end of this split's range
 };
 
-__device__ inline SegmentWalk begin_walk(const int32_t* __restrict__ seqlens, int B, int64_t g, const Plan& p) {
+__device__ inline SegmentWalk begin_walk(const Lens& s, int64_t g, const Plan& p) {
   SegmentWalk w;
   w.cur = split_begin(g, p);
   w.end = split_begin(g + 1, p);
-  find_sequence(seqlens, B, w.cur, w.b, w.Pb);
+  find_sequence(s, w.cur, w.b, w.Pb);
   return w;
 }
 
-// Next (sequence, first tile, end tile) of the split, tiles local to the sequence.
-__device__ inline bool next_segment(const int32_t* __restrict__ seqlens, int B, SegmentWalk& w, int& b, int& ta,
-                             int& te) {
-  while (w.cur < w.end && w.b < B) {
-    const int64_t n = tiles_of(seqlens[w.b]);
+// Next (sequence, first tile, end tile) of the split, tiles local to the sequence, and the
+// sequence's length L.
+__device__ inline bool next_segment(const Lens& s, SegmentWalk& w, int& b, int& ta, int& te, int& L) {
+  while (w.cur < w.end && w.b < s.B) {
+    const int len = len_of(s, __builtin_amdgcn_readfirstlane(w.b));
+    const int64_t n = tiles_of(len);
     const int64_t seg_end = w.end < w.Pb + n ? w.end : w.Pb + n;
     if (n > 0 && w.cur < seg_end) {
       b = w.b;
       ta = int(w.cur - w.Pb);
       te = int(seg_end - w.Pb);
+      L = len;
       w.cur = seg_end;
       if (seg_end == w.Pb + n) {
         w.Pb += n;

@@ -17,15 +17,16 @@ __global__ __launch_bounds__(64) void plan_kernel(const int32_t* seqlens, int B,
   const int lane = threadIdx.x;
   int32_t* row = out + int64_t(g) * max_seg * 3;
   for (int k = lane; k < max_seg * 3; k += 64) row[k] = -1;
-  const Plan plan = make_plan(seqlens, B, G_req);
+  const Lens lens = load_lens(seqlens, B);
+  const Plan plan = make_plan(lens, G_req);
   if (g == 0 && lane == 0) {
     out[int64_t(G_req) * max_seg * 3] = int32_t(plan.T);
     out[int64_t(G_req) * max_seg * 3 + 1] = plan.G;
   }
   if (g >= plan.G) return;
-  SegmentWalk walk = begin_walk(seqlens, B, g, plan);
-  int b, ta, te, k = 0;
-  while (next_segment(seqlens, B, walk, b, ta, te)) {
+  SegmentWalk walk = begin_walk(lens, g, plan);
+  int b, ta, te, L, k = 0;
+  while (next_segment(lens, walk, b, ta, te, L)) {
     if (lane == 0 && k < max_seg) {
       row[3 * k] = b;
       row[3 * k + 1] = ta;
