@@ -188,14 +188,16 @@ def cpu_baseline(inp, target_s):
     one = time.perf_counter() - t0
     n = max(1, min(B, int(target_s / max(one, 1e-3))))
     sel = list(range(n))
-    # When the whole batch fits the time budget, repeat it to fill the budget (up to 7 runs) and take
-    # the median.
-    runs = max(1, min(7, int(target_s / max(one * n, 1e-3)))) if n == B else 1
+    # When the whole batch fits the time budget, repeat it until the budget is spent (up to 7 runs)
+    # and take the median.
     els = []
-    for _ in range(runs):
+    while True:
         t0 = time.perf_counter()
         oracle.decode_inputs(inp, batch_indices=sel)
         els.append(time.perf_counter() - t0)
+        if n < B or len(els) >= 7 or sum(els) + els[-1] > target_s:
+            break
+    runs = len(els)
     el = sorted(els)[len(els) // 2]
     tok_sample = sum(Ls[b] for b in sel)
     per_step_s = el * (sum(Ls) / max(tok_sample, 1))
