@@ -167,7 +167,8 @@ def test_split_counts_agree():
 
 
 def test_plan_partitions_tiles():
-    """Split planning (integer): every tile of every sequence exactly once, in order; splits balanced."""
+    """Split planning (integer, exact): split g holds exactly the global tiles [g*T/G, (g+1)*T/G);
+    every tile of every sequence exactly once, in order."""
     mlra = _mlra()
     rng = np.random.default_rng(0)
     for trial in range(12):
@@ -178,18 +179,19 @@ def test_plan_partitions_tiles():
         seqlens = torch.tensor(Ls, dtype=torch.int32, device="cuda")
         segs, T, G = mlra.plan(seqlens, G_req, max_segments=B + 1)
         tiles = [(int(L) + 31) // 32 for L in Ls]
+        first = np.concatenate([[0], np.cumsum(tiles)])  # first global tile of each sequence
         assert T == sum(tiles) and G == min(G_req, T)
         seen = []
         for g in range(G_req):
-            n = 0
+            flat = []
             for (b, ta, te) in segs[g].tolist():
                 if b < 0:
                     continue
                 assert g < G and 0 <= ta < te <= tiles[b]
                 seen += [(b, t) for t in range(ta, te)]
-                n += te - ta
-            if g < G:
-                assert n in (T // G, -(-T // G))
+                flat += [int(first[b]) + t for t in range(ta, te)]
+            if g < G:  # exactly the global tiles [g*T/G, (g+1)*T/G)
+                assert flat == list(range(g * T // G, (g + 1) * T // G))
         assert seen == [(b, t) for b in range(B) for t in range(tiles[b])]
 
 
