@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "mlra_device.h"
 
@@ -15,8 +16,9 @@ namespace {
 // ------------------------------------------------------------------ combine kernel
 //
 // One workgroup per (query head i, block q of kCombBlock of the NB * d_latent latent channels
-// (512, or 128 in the shard form), group of up to 32 sequences). Block q lies in latent head j = q*kCombBlock / d_latent, channels
-// c0..c0+kCombBlock-1 of it, c0 = q*kCombBlock % d_latent.
+// (512, or 128 in the shard form), run of `sub` sequences). Block q lies in latent head j =
+// q*kCombBlock / d_latent, channels c0..c0+kCombBlock-1 of it, c0 = q*kCombBlock % d_latent.
+// The runs tile the 32-sequence groups of the ypart layout (sub is 32, 16, 8 or 4).
 //  1. merge:   obar[b][k] = sum_s 2^{m_s-M} O_s[c0+k] / sum_s 2^{m_s-M} l_s over the splits
 //              s holding part of sequence b (slots g + b, g in [g_first, g_last]), into LDS.
 //  2. project: y_q[b][d] = sum_k obar[b][k] * W_UV[j][i][c0+k][d] on fp32 MFMA
@@ -35,6 +37,7 @@ struct CombineArgs {
   float* ypart;    // [groups][h][nblk][32][128]
   int B, h;
   int nblk;        // kCombBlock-channel blocks of the NB * d_latent latent channels
+  int sub;         // sequences per workgroup: a power of two dividing kCombSeqs
 };
 
 constexpr int kCombSeqs = 32;
@@ -76,11 +79,12 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int wave = tid >> 6;
   const int i = blockIdx.x;
   const int q = blockIdx.y;
-  const int grp = blockIdx.z;
+  const int b0 = blockIdx.z * a.sub;  // first sequence of this workgroup's run
+  const int grp = b0 / kCombSeqs;       // its 32-sequence group ...
+  const int s0 = b0 % kCombSeqs;        // ... and its first row there
   const int j = (q * kCombBlock) / DL;
   const int c0 = (q * kCombBlock) % DL;
-  const int b0 = grp * kCombSeqs;
-  const int nb = min(kCombSeqs, a.B - b0);
+  const int nb = min(a.sub, a.B - b0);
   const int n = lane & 31, hh = lane >> 5;
 
   // The W_UV slice this wave multiplies by (rows c0 + 2kb + hh, column 32*wave + n), issued
@@ -167,22 +171,28 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
     for (int v = 0; v < 4; ++v) {
       const int k = 4 * (cq0 + kCombTPS * v);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ob[k + e][bl] = live ? st.acc[v][e] * inv : 0.f;
+      for (int e = 0; e < 4; ++e) ob[k + e][s0 + bl] = live ? st.acc[v][e] * inv : 0.f;
     }
   }
-  // Sequences of the padded group beyond nbp read as zero.
-  for (int idx = tid; idx < kCombBlock * kCombSeqs; idx += 256)
-    if ((idx % kCombSeqs) >= nbp) ob[idx / kCombSeqs][idx % kCombSeqs] = 0.f;
+  // Rows of the 32-sequence group outside this run read as zero (their outputs are not stored).
+  for (int idx = tid; idx < kCombBlock * kCombSeqs; idx += 256) {
+    const int col = idx % kCombSeqs;
+    if (col < s0 || col >= s0 + nbp) ob[idx / kCombSeqs][col] = 0.f;
+  }
   __syncthreads();
 
-  // ---- 2. project: wave w computes output channels [32w, 32w+32) for all 32 sequences.
+  // ---- 2. project: wave w computes output channels [32w, 32w+32) for the group's 32 rows;
+  // the rows of this run are stored.
   floatx16 y = {};
 #pragma unroll
   for (int kb = 0; kb < kSteps; ++kb) y = __builtin_amdgcn_mfma_f32_32x32x2f32(ob[2 * kb + hh][n], wv[kb], y, 0, 0, 0);
 
   float* yq = a.ypart + ((int64_t(grp) * a.h + i) * a.nblk + q) * (kCombSeqs * kDV);
 #pragma unroll
-  for (int rr = 0; rr < 16; ++rr) yq[(8 * (rr >> 2) + 4 * hh + (rr & 3)) * kDV + 32 * wave + n] = y[rr];
+  for (int rr = 0; rr < 16; ++rr) {
+    const int row = 8 * (rr >> 2) + 4 * hh + (rr & 3);
+    if (unsigned(row - s0) < unsigned(nb)) yq[row * kDV + 32 * wave + n] = y[rr];
+  }
 }
 
 // out[b][i][:] = out_scale * (y_0 + y_1 + ...)[b][:], blocks added in this order.
@@ -210,6 +220,42 @@ __global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
 #pragma unroll
   for (int qq = 1; qq < NBLK; ++qq) v += y[qq * kBlk];
   reinterpret_cast<floatx4*>(a.out)[idx] = a.out_scale * v;
+}
+
+// Sequences per combine workgroup: 32 (or B rounded up to a power of two, at least 4),
+// halved while the grid holds fewer workgroups than the device has compute units. The
+// one-latent-head shard form has a quarter of the channel blocks, so its 32 query heads give
+// 64 workgroups at 32 sequences and 256 at 8. Measured on MI355X, B=32, h=32, L=32K, whole
+// steps: the shard form 83.4 us at 32 sequences, 80.6 at 8; MLRA-4 and MLA, whose grids
+// already fill the device, lose 2 us or more at 16 (each run then reads the W_UV slices again).
+int combine_sub(int B, int h, int nblk, int cus) {
+  int sub = 4;
+  while (sub < kCombSeqs && sub < B) sub <<= 1;
+  while (sub > 4 && int64_t(h) * nblk * ((B + sub - 1) / sub) < cus) sub >>= 1;
+  return sub;
+}
+
+// Compute units of the current device, cached per device.
+int device_cus(int* cus) {
+  static std::mutex mu;
+  static int cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev >= 0 && dev < 64) {
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache[dev] > 0) {
+      *cus = cache[dev];
+      return MLRA_OK;
+    }
+  }
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+  if (dev >= 0 && dev < 64) {
+    std::lock_guard<std::mutex> lk(mu);
+    cache[dev] = *cus;
+  }
+  return MLRA_OK;
 }
 
 using CombineFn = void (*)(CombineArgs);
@@ -252,7 +298,11 @@ extern "C" int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, fl
   c.B = p->batch;
   c.h = p->num_heads;
   c.nblk = latent_total(*p) / kCombBlock;
-  const dim3 grid(p->num_heads, c.nblk, (p->batch + kCombSeqs - 1) / kCombSeqs);
+  int cus = 0;
+  rc = device_cus(&cus);
+  if (rc) return rc;
+  c.sub = combine_sub(p->batch, p->num_heads, c.nblk, cus);
+  const dim3 grid(p->num_heads, c.nblk, (p->batch + c.sub - 1) / c.sub);
   hipLaunchKernelGGL(pick_combine(p->num_branches, p->d_latent), grid, dim3(256), 0,
                      static_cast<hipStream_t>(stream), c);
   hipError_t e = hipGetLastError();
