@@ -301,6 +301,20 @@ def test_two_sequence_groups_and_workspace_reuse():
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
 
 
+@pytest.mark.parametrize("cfg,B,h", [(7, 40, 32), (2, 45, 4)])
+def test_combine_runs_across_groups(cfg, B, h):
+    """Batches past one 32-sequence group whose combine grid alone would not fill the device, so a
+    combine workgroup takes a shorter run of sequences: runs of 8 for the shard form at B=40, h=32,
+    of 4 for MLRA-4 at B=45, h=4 (the last run holds one sequence)."""
+    rng = np.random.default_rng(43 + B)
+    Ls = tuple(int(x) for x in rng.integers(0, 700, size=B))
+    w = WORKLOADS[cfg].replace(B=B, h=h, lengths=("list", Ls))
+    inp = make_inputs(w, seed=43, poison=True)
+    print(f"{w.name} B={B} h={h}", flush=True)
+    got = gpu_decode(inp, 0)
+    assert_parity(got, oracle.decode_inputs(inp), label=f"{w.name} B={B} h={h}")
+
+
 def test_one_sequence_of_a_million_tokens():
     """Maximum length on one GPU-resident sequence: B=1, L=2^20 (1.2 GB of cache). Every split
     of the default launch falls in the same sequence, so the combine merges 512+1 slots for it."""
