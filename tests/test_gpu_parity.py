@@ -338,11 +338,13 @@ def test_a_thousand_short_sequences():
         assert_parity(got, oracle.decode_inputs(inp), label=f"B=1000 {w.name} page={w.page_size}")
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("cfg", [5, 7, 4])
+def test_graph_replay_matches_eager(cfg):
     """A captured decode step replayed several times, with eager work in between, gives the
-    eager result every time (the step records kernel launches only)."""
+    eager result every time (the step records kernel launches only): paged MLRA-4, the shard form
+    (whose combine runs over short sequence runs) and MLA."""
     mlra = _mlra()
-    w = WORKLOADS[5].replace(B=6, lengths=("list", (700, 1, 2048, 65, 0, 333)))
+    w = WORKLOADS[cfg].replace(B=6, lengths=("list", (700, 1, 2048, 65, 0, 333)))
     inp = make_inputs(w, seed=12)
     d = inp.to("cuda")
     dec = mlra.Decoder(d.q_nope, d.q_rope, d.latent, d.rope, seqlens=d.seqlens, W_UV=d.W_UV, sm_scale=w.sm_scale,
@@ -358,7 +360,7 @@ def test_graph_replay_matches_eager():
         assert torch.equal(dec.out, eager), f"replay {k}"
         junk = torch.randn(1 << 16, device="cuda").sum()  # eager work between replays
         torch.cuda.synchronize()
-    assert_parity(eager.cpu().double().numpy(), oracle.decode_inputs(inp), label="graph")
+    assert_parity(eager.cpu().double().numpy(), oracle.decode_inputs(inp), label=f"graph cfg{cfg}")
 
 
 def test_two_streams_two_workspaces():
