@@ -8,6 +8,13 @@ One step = one full decode of the workload's batch through the C ABI
 
 Prints one JSON line. `value` is microseconds per step (lower is better) for the
 workload the headline metric is quoted on (B=32, h=32, L=32768, MLRA-4, bf16).
+
+Order: W untimed warm-up steps, then a settle phase of back-to-back steps (at least
+--settle-min-ms, until three consecutive 20-step windows agree within 1.5 %, at most
+--settle-max-ms; reported as `settle`), then the K timed steps. On MI355X the step runs
+15-45 % slow for 25-45 ms after any change of load (a fresh process, an idle gap of
+20 ms or more, a burst of other kernels) whatever the shader clock reads; the settle
+phase waits that out without depending on W.
 """
 from __future__ import annotations
 
@@ -35,9 +42,11 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=2000,
-                    help="untimed steps first: on MI355X the whole-step time settles only after about 40 ms "
-                         "of back-to-back work (about 200 steps at the headline shape), 25 %% above steady before")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps before the settle phase")
+    ap.add_argument("--settle-min-ms", type=float, default=100.0,
+                    help="settle phase: back-to-back steps for at least this long before timing")
+    ap.add_argument("--settle-max-ms", type=float, default=1000.0,
+                    help="settle phase: stop after this long even if the windows still disagree")
     ap.add_argument("--config", type=int, default=2, help="workload number (1-7); 2 is the headline")
     ap.add_argument("--num-splits", type=int, default=0, help="0 = one split per resident workgroup slot")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -45,6 +54,10 @@ def parse():
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="also time steps each preceded by a write of this many MiB (cold L2 / Infinity Cache); 0 = skip")
     ap.add_argument("--copy-probe-mib", type=int, default=1024, help="size of the copy-kernel reference run")
+    ap.add_argument("--record-mfma", metavar="COUNTER_CSV",
+                    help="no GPU: turn a rocprofv3 --pmc counter CSV (SQ_INSTS_VALU_MFMA_MOPS_BF16, "
+                         "SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE) of this benchmark into the per-launch "
+                         "MFMA record under profiles/")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of this "
                          "benchmark into the per-launch HBM traffic record under profiles/")
@@ -140,6 +153,81 @@ def record_traffic(fetch_csv, write_csv, args):
     print(json.dumps(rec))
 
 
+def settle(step, min_ms, max_ms, window=20, tol=0.015):
+    """Back-to-back calls of step() in windows of `window`, each ended by a device synchronisation,
+    until at least min_ms have passed and the last three window means agree within tol (relative
+    to the smallest), or max_ms have passed. Returns what it saw."""
+    import torch
+    means = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        for _ in range(window):
+            step()
+        torch.cuda.synchronize()
+        means.append((time.perf_counter() - t0) * 1e6 / window)
+        el = (time.perf_counter() - t_start) * 1e3
+        last = means[-3:]
+        agreed = len(means) >= 3 and max(last) - min(last) <= tol * min(last)
+        if el >= max_ms or (el >= min_ms and agreed):
+            break
+    return {"settle_ms": round(el, 1), "windows": len(means), "window_steps": window, "agreed": agreed,
+            "first_window_us": round(means[0], 2), "last_windows_us": [round(x, 2) for x in last]}
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def mfma_record(workload_name):
+    """Counter-measured MFMA work per attention-kernel launch, valid only for the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"mfma_decode_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec
+
+
+def record_mfma(counter_csv, args):
+    """Per-launch means of the attention kernel's MFMA counters. SQ_INSTS_VALU_MFMA_MOPS_BF16 counts
+    bf16 MFMA work in units of 512 FLOP; SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of every SIMD;
+    GRBM_GUI_ACTIVE comes summed over the 8 XCDs (one count per XCD), so the busy fraction is
+    busy / (GRBM_GUI_ACTIVE / 8 * SIMDs), the expression rocprofv3 uses for MfmaUtil."""
+    import csv
+    from mlra_workloads import WORKLOADS, make_inputs
+    acc, spans = {}, {}
+    for r in csv.DictReader(open(counter_csv)):
+        k = r["Kernel_Name"]
+        if not re.search(r"decode_(branch_|hs_|shard_)?kernel", k):
+            continue
+        acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        spans[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+        kname = k.split("(")[0]
+    mean = {c: sum(v) / len(v) for c, v in acc.items()}
+    w = WORKLOADS[args.config]
+    inp = make_inputs(w, seed=args.config)
+    us = sum(spans.values()) / len(spans)
+    flops = mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    algo = flop_per_head_token(w) * w.h * inp.total_tokens
+    simds = 1024
+    busy_frac = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (mean["GRBM_GUI_ACTIVE"] / 8 * simds)
+    rec = {"workload": w.name, "kernel": kname, "launches": len(spans),
+           "mfma_bf16_flop_per_launch": round(flops), "algorithmic_flop_per_launch": algo,
+           "executed_over_algorithmic": round(flops / algo, 4),
+           "mfma_busy_cycles_per_launch": round(mean["SQ_VALU_MFMA_BUSY_CYCLES"]),
+           "grbm_gui_active_per_launch": round(mean["GRBM_GUI_ACTIVE"]),
+           "mfma_busy_frac": round(busy_frac, 4),
+           "avg_launch_us_under_profiler": round(us, 2),
+           "executed_TFLOPs": round(flops / (us * 1e-6) / 1e12, 1),
+           "executed_frac_of_bf16_peak": round(flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+           "counters": list(MFMA_COUNTERS), "simds": simds,
+           "kernel_sources": list(KERNEL_SOURCES), "kernel_source_sha256": kernel_source_hash()}
+    out = os.path.join(ROOT, "profiles", f"mfma_decode_{w.name}.json")
+    json.dump(rec, open(out, "w"), indent=1)
+    print(json.dumps(rec))
+
+
 def gqa_leg(mlra, inp, args, stream, mlra_ms, shard=False):
     """The GQA decode comparator at the pages' GQA shape (64 query heads over 8 KV heads of
     128 channels) on the same batch and lengths as the MLRA workload; inputs drawn on the GPU.
@@ -155,7 +243,7 @@ def gqa_leg(mlra, inp, args, stream, mlra_ms, shard=False):
     dec = mlra.GqaDecoder(gi.q, gi.k_cache, gi.v_cache, seqlens=sl, sm_scale=g.sm_scale, max_seqlen=gi.max_seqlen)
     for _ in range(args.warmup):
         dec(stream)
-    torch.cuda.synchronize()
+    st = settle(lambda: dec(stream), args.settle_min_ms / 2, args.settle_max_ms)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         dec(stream)
@@ -170,7 +258,9 @@ def gqa_leg(mlra, inp, args, stream, mlra_ms, shard=False):
             "cache_bytes": cb, "cache_GBps": round(cb / (us * 1e-6) / 1e9, 1),
             "hbm_frac": round(cb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
             "gqa_over_mlra_step_time": round(us / (mlra_ms * 1e3), 3),
-            "timing": "eager launches (attention + merge), K steps between two device synchronisations"}
+            "settle": st,
+            "timing": "eager launches (attention + merge), K steps between two device synchronisations, "
+                      "after its own settle phase"}
 
 
 def cpu_baseline(inp, target_s):
@@ -237,6 +327,9 @@ def main():
     if args.record_traffic:
         record_traffic(*args.record_traffic, args)
         return
+    if args.record_mfma:
+        record_mfma(args.record_mfma, args)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}). One GPU's share "
@@ -260,8 +353,93 @@ def main():
                        sm_scale=w.sm_scale, out_scale=w.gamma, max_seqlen=inp.max_seqlen,
                        block_table=d.block_table, page_size=w.page_size, num_splits=args.num_splits)
     stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    # Copy-kernel reference (achievable bandwidth; also the calibration kernel for byte counters).
+    print(f"bench: {args.warmup} warmup steps, settle phase, {args.steps} timed steps, splits={dec.splits}",
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        dec(stream)
+    torch.cuda.synchronize()
+    st = settle(lambda: dec(stream), args.settle_min_ms, args.settle_max_ms)
+    print(f"bench: settled after {st['settle_ms']} ms: {st['last_windows_us']} us/step", file=sys.stderr,
+          flush=True)
+
+    # Headline: K back-to-back steps through the C ABI between two device synchronisations.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dec(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # Per-kernel durations in the same settled state: K more steps, each with HIP events on the
+    # launch stream around its attention launch and its combine launches. An event between
+    # launches idles the GPU for a moment, so these read slightly high.
+    evs = [[ev() for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        evs[k][0].record(stream)
+        dec.splitkv(stream)
+        evs[k][1].record(stream)
+        dec.combine(stream)
+        evs[k][2].record(stream)
+    torch.cuda.synchronize()
+    ev_step_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    dk = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    ck = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    dk_mean = sum(dk) / len(dk)
+    ck_mean = sum(ck) / len(ck)
+
+    # Cold caches: before each step an untimed write of flush_mib MiB evicts L2 and the
+    # Infinity Cache, then events bracket the whole step.
+    cold = None
+    if args.flush_mib > 0:
+        junk = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev)
+        cev = [(ev(), ev()) for _ in range(args.steps)]
+        for k in range(args.steps):
+            junk.fill_(float(k))
+            cev[k][0].record(stream)
+            dec(stream)
+            cev[k][1].record(stream)
+        torch.cuda.synchronize()
+        cold = sorted(a.elapsed_time(b) for a, b in cev)
+        del junk
+    graph = None
+    if args.graph:
+        # The same step recorded once as a HIP graph and replayed: the way a serving loop runs it.
+        g = dec.capture_graph()
+        gst = settle(g.replay, args.settle_min_ms / 2, args.settle_max_ms)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph = {"us_per_step": round((time.perf_counter() - t0) * 1e6 / args.steps, 2), "settle": gst}
+    absorb = None
+    if args.absorb:
+        from mlra_workloads import make_absorption_inputs
+        q_pre, W_UK = make_absorption_inputs(w, seed=args.config, B=len(inp.seqlens))
+        q_pre, W_UK = q_pre.to(dev), W_UK.to(dev)
+        qn = torch.empty(len(inp.seqlens), w.h, w.NB, w.DL, dtype=w.torch_dtype, device=dev)
+        absorber = mlra.Absorber(q_pre, W_UK, qn)
+        for _ in range(3):
+            absorber(stream)
+        ea = [ev() for _ in range(2)]
+        ea[0].record(stream)
+        for _ in range(args.steps):
+            absorber(stream)
+        ea[1].record(stream)
+        torch.cuda.synchronize()
+        a_us = ea[0].elapsed_time(ea[1]) * 1e3 / args.steps
+        a_bytes = q_pre.numel() * q_pre.element_size() + W_UK.numel() * 4 + qn.numel() * qn.element_size()
+        absorb = {"us_per_call": round(a_us, 2), "algorithmic_bytes": a_bytes,
+                  "achieved_GBps": round(a_bytes / (a_us * 1e-6) / 1e9, 1)}
+    gqa = None
+    if not args.no_gqa and w.dtype == "bf16" and w.page_size == 0:
+        gqa = gqa_leg(mlra, inp, args, stream, ms_per_step, shard=(w.NB == 1 and w.DL == 128))
+
+    # Copy-kernel reference (achievable bandwidth; also the calibration kernel for byte counters),
+    # last, so that its load pattern does not precede the measurements above.
     copy_gbps = read_gbps = None
     if args.copy_probe_mib > 0:
         nbytes = args.copy_probe_mib << 20
@@ -269,7 +447,7 @@ def main():
         dst = torch.empty_like(src)
         for _ in range(3):
             mlra.copy_bandwidth_probe(src, dst)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = ev(), ev()
         e0.record(stream)
         for _ in range(10):
             mlra.copy_bandwidth_probe(src, dst)
@@ -287,108 +465,20 @@ def main():
         read_gbps = nbytes * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         del src, dst
 
-    print(f"bench: {args.warmup} warmup + {args.steps} timed steps, splits={dec.splits}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        dec(stream)
-    torch.cuda.synchronize()
-
-    # Headline: K back-to-back steps through the C ABI between two device synchronisations.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        dec(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    eager_ms = (t1 - t0) * 1e3 / args.steps
-    ms_per_step = eager_ms
-
-    # Per-kernel durations, from HIP events on the launch stream. (1) The attention kernel
-    # launched K times back to back and the combine (combine + finalize) K times back to back,
-    # each run bracketed by one event pair: the mean launch duration. (2) Every step bracketed
-    # by its own events, for the spread; an event between launches idles the GPU for a few
-    # microseconds, so these per-launch figures run slightly high.
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    ea, eb, ec = ev(), ev(), ev()
-    ea.record(stream)
-    for _ in range(args.steps):
-        dec.splitkv(stream)
-    eb.record(stream)
-    for _ in range(args.steps):
-        dec.combine(stream)
-    ec.record(stream)
-    torch.cuda.synchronize()
-    dk_mean = ea.elapsed_time(eb) / args.steps
-    ck_mean = eb.elapsed_time(ec) / args.steps
-    evs = [[ev() for _ in range(3)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        evs[k][0].record(stream)
-        dec.splitkv(stream)
-        evs[k][1].record(stream)
-        dec.combine(stream)
-        evs[k][2].record(stream)
-    torch.cuda.synchronize()
-    # (3) Cold caches: before each step an untimed write of flush_mib MiB evicts L2 and the
-    # Infinity Cache, then events bracket the whole step.
-    cold = None
-    if args.flush_mib > 0:
-        junk = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev)
-        cev = [(ev(), ev()) for _ in range(args.steps)]
-        for k in range(args.steps):
-            junk.fill_(float(k))
-            cev[k][0].record(stream)
-            dec(stream)
-            cev[k][1].record(stream)
-        torch.cuda.synchronize()
-        cold = sorted(a.elapsed_time(b) for a, b in cev)
-        del junk
-    graph_ms = None
-    if args.graph:
-        # The same step recorded once as a HIP graph and replayed: the way a serving loop runs it.
-        graph = dec.capture_graph()
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    absorb = None
-    if args.absorb:
-        from mlra_workloads import make_absorption_inputs
-        q_pre, W_UK = make_absorption_inputs(w, seed=args.config, B=len(inp.seqlens))
-        q_pre, W_UK = q_pre.to(dev), W_UK.to(dev)
-        qn = torch.empty(len(inp.seqlens), w.h, w.NB, w.DL, dtype=w.torch_dtype, device=dev)
-        absorber = mlra.Absorber(q_pre, W_UK, qn)
-        for _ in range(3):
-            absorber(stream)
-        ea = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ea[0].record(stream)
-        for _ in range(args.steps):
-            absorber(stream)
-        ea[1].record(stream)
-        torch.cuda.synchronize()
-        a_us = ea[0].elapsed_time(ea[1]) * 1e3 / args.steps
-        a_bytes = q_pre.numel() * q_pre.element_size() + W_UK.numel() * 4 + qn.numel() * qn.element_size()
-        absorb = {"us_per_call": round(a_us, 2), "algorithmic_bytes": a_bytes,
-                  "achieved_GBps": round(a_bytes / (a_us * 1e-6) / 1e9, 1)}
-    gqa = None
-    if not args.no_gqa and w.dtype == "bf16" and w.page_size == 0:
-        gqa = gqa_leg(mlra, inp, args, stream, ms_per_step, shard=(w.NB == 1 and w.DL == 128))
-    dk = sorted(e[0].elapsed_time(e[1]) for e in evs)
-
     ab = algorithmic_bytes(inp)
     tokens = inp.total_tokens
     flops = flop_per_head_token(w) * w.h * tokens + 2 * len(inp.seqlens) * w.h * w.NB * w.DL * w.DV
     us = ms_per_step * 1e3
     achieved = ab["attention"] / (dk_mean * 1e-3) / 1e9
     trec = traffic_record(w.name)
+    mrec = mfma_record(w.name)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": (trec["hbm_bytes_per_launch"] if trec else None),
                 "kernel": attention_kernel_name(w) + " (split-KV attention)",
                 "algorithmic_bytes_per_launch": ab["attention"],
-                "avg_launch_us": round(dk_mean * 1e3, 2)}
+                "avg_launch_us": round(dk_mean * 1e3, 2),
+                "timing": "HIP events on the launch stream around each attention launch of K settled steps"}
     result = {
         "metric": METRIC, "value": round(us, 2), "unit": "µs/step", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": False,
@@ -397,19 +487,28 @@ def main():
                    "d_latent": w.DL, "d_rope": w.DR, "d_v": w.DV, "seq_len": inp.max_seqlen,
                    "cached_tokens": tokens, "page_size": w.page_size, "num_splits": dec.splits,
                    "parallelism": "none (one GPU)"},
-        "timing": "eager launches through the C ABI, K steps between two device synchronisations",
-        "graph_replay_us_per_step": None if graph_ms is None else round(graph_ms * 1e3, 2),
+        "timing": "eager launches through the C ABI, K steps between two device synchronisations, "
+                  "after W warm-up steps and a settle phase",
+        "settle": st,
         "achieved_hbm_TBps": round(ab["step"] / (us * 1e-6) / 1e12, 3),
+        "hbm_frac_step": round(ab["step"] / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "tokens_per_s": round(len(inp.seqlens) / (us * 1e-6), 1),
         "mfma_frac": round(flops / (us * 1e-6) / 1e12 / MFMA_PEAK_TFLOPS[w.dtype], 4),
+        "mfma_counters": None if mrec is None else {
+            k: mrec[k] for k in ("mfma_busy_frac", "executed_frac_of_bf16_peak", "executed_over_algorithmic",
+                                 "mfma_bf16_flop_per_launch", "avg_launch_us_under_profiler")},
         "kernels_us": {"attention_kernel_mean": round(dk_mean * 1e3, 2),
-                       "attention_kernel_p10_event_bracketed": round(dk[len(dk) // 10] * 1e3, 2),
-                       "attention_kernel_p90_event_bracketed": round(dk[(9 * len(dk)) // 10] * 1e3, 2),
-                       "combine_and_finalize_mean": round(ck_mean * 1e3, 2)},
+                       "attention_kernel_p10": round(dk[len(dk) // 10] * 1e3, 2),
+                       "attention_kernel_p90": round(dk[(9 * len(dk)) // 10] * 1e3, 2),
+                       "combine_mean": round(ck_mean * 1e3, 2),
+                       "combine_p10": round(ck[len(ck) // 10] * 1e3, 2),
+                       "combine_p90": round(ck[(9 * len(ck)) // 10] * 1e3, 2),
+                       "step_with_events": round(ev_step_ms * 1e3, 2)},
         "cold_cache_us_per_step": None if cold is None else {
             "median": round(cold[len(cold) // 2] * 1e3, 2), "p10": round(cold[len(cold) // 10] * 1e3, 2),
             "p90": round(cold[(9 * len(cold)) // 10] * 1e3, 2),
             "note": f"each step after an untimed {args.flush_mib} MiB write, events around the step"},
+        "graph_replay": graph,
         "algorithmic_bytes_per_step": ab["step"],
         "copy_probe_GBps": None if copy_gbps is None else round(copy_gbps, 1),
         "read_probe_GBps": None if read_gbps is None else round(read_gbps, 1),

@@ -42,6 +42,10 @@ def make_params(q_nope: torch.Tensor, q_rope: torch.Tensor, latent_cache: torch.
     q_nope [B, h, NB, DL], q_rope [B, h, DR], latent_cache [rows, NB, DL], rope_cache [rows, DR]:
     the innermost row of each must be contiguous (views into joint tensors are fine).
     """
+    if q_nope.dim() != 4:
+        raise ValueError(f"q_nope must be [B, h, NB, d_latent] (got {list(q_nope.shape)})")
+    if q_rope.dim() != 3 or latent_cache.dim() != 3 or rope_cache.dim() != 2:
+        raise ValueError("q_rope must be [B, h, d_rope], latent_cache [rows, NB, d_latent], rope_cache [rows, d_rope]")
     B, h, NB, DL = q_nope.shape
     if q_nope.stride(3) != 1 or q_nope.stride(2) != DL:
         raise ValueError("q_nope rows [NB, DL] must be contiguous")
@@ -61,6 +65,69 @@ def make_params(q_nope: torch.Tensor, q_rope: torch.Tensor, latent_cache: torch.
     p.lat_stride_tok, p.rope_stride_tok = latent_cache.stride(0), rope_cache.stride(0)
     p.sm_scale, p.out_scale = sm_scale, out_scale
     return p
+
+
+def _same_gpu(tensors, names) -> None:
+    """Every tensor given must live on one and the same GPU."""
+    devs = {t.device for t in tensors if t is not None}
+    bad = [n for t, n in zip(tensors, names) if t is not None and t.device.type != "cuda"]
+    if bad:
+        raise ValueError(f"{', '.join(bad)} must be GPU tensors")
+    if len(devs) > 1:
+        raise ValueError(f"{', '.join(names)} must all be on one GPU (got {sorted(str(d) for d in devs)})")
+
+
+def _check_meta(seqlens, block_table, B: int, paged: bool, max_seqlen: int, page_size: int) -> None:
+    if seqlens is None or seqlens.dtype != torch.int32 or not seqlens.is_contiguous() or seqlens.dim() != 1 \
+            or seqlens.numel() != B:
+        raise ValueError(f"seqlens must be a contiguous int32 tensor of shape [{B}]")
+    if paged:
+        if block_table is None or block_table.dtype != torch.int32 or not block_table.is_contiguous() \
+                or block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError(f"block_table must be a contiguous int32 tensor of shape [{B}, max_pages_per_seq]")
+        if block_table.shape[1] * page_size < max_seqlen:
+            raise ValueError(f"block_table has {block_table.shape[1]} columns of {page_size} tokens, fewer than "
+                             f"max_seqlen = {max_seqlen} tokens")
+    elif block_table is not None:
+        raise ValueError("block_table is given but page_size is 0")
+
+
+def _check_cache_rows(rows: int, B: int, max_seqlen: int, paged: bool, page_size: int, what: str) -> None:
+    """Rows the kernels may address: B * max_seqlen for a contiguous cache; for a paged pool at least one
+    page (the block-table entries themselves are device data, which the C ABI leaves unchecked)."""
+    if not paged and rows < B * max_seqlen:
+        raise ValueError(f"{what} has {rows} rows; a contiguous cache of {B} sequences needs B * max_seqlen = "
+                         f"{B * max_seqlen}")
+    if paged and B > 0 and rows < page_size:
+        raise ValueError(f"{what} has {rows} rows, less than one page of {page_size}")
+
+
+def _check_decode_tensors(p: DecodeParams, q_nope, q_rope, latent_cache, rope_cache, seqlens, W_UV, block_table,
+                          out) -> None:
+    """Host-side shape, dtype and layout checks of everything a decode launch reads or writes, so that
+    a mismatched tensor raises here instead of sending the kernels out of bounds."""
+    B, h, NB, DL = p.batch, p.num_heads, p.num_branches, p.d_latent
+    if tuple(q_rope.shape) != (B, h, p.d_rope):
+        raise ValueError(f"q_rope must be [{B}, {h}, {p.d_rope}] (got {list(q_rope.shape)})")
+    if latent_cache.dim() != 3 or tuple(latent_cache.shape[1:]) != (NB, DL):
+        raise ValueError(f"latent_cache must be [rows, {NB}, {DL}] (got {list(latent_cache.shape)})")
+    if rope_cache.dim() != 2 or rope_cache.shape[1] != p.d_rope:
+        raise ValueError(f"rope_cache must be [rows, {p.d_rope}] (got {list(rope_cache.shape)})")
+    if rope_cache.shape[0] != latent_cache.shape[0]:
+        raise ValueError(f"latent_cache ({latent_cache.shape[0]} rows) and rope_cache ({rope_cache.shape[0]} rows) "
+                         "must share one row numbering")
+    paged = p.page_size > 0
+    _check_cache_rows(latent_cache.shape[0], B, p.max_seqlen, paged, p.page_size, "latent_cache")
+    _check_meta(seqlens, block_table, B, paged, p.max_seqlen, p.page_size)
+    if W_UV is None or W_UV.dtype != torch.float32 or not W_UV.is_contiguous() \
+            or tuple(W_UV.shape) != (NB, h, DL, p.d_v):
+        raise ValueError(f"W_UV must be a contiguous float32 tensor [{NB}, {h}, {DL}, {p.d_v}]"
+                         + ("" if W_UV is None else f" (got {W_UV.dtype} {list(W_UV.shape)})"))
+    if out is not None and (out.dtype != torch.float32 or not out.is_contiguous()
+                            or tuple(out.shape) != (B, h, p.d_v)):
+        raise ValueError(f"out must be a contiguous float32 tensor [{B}, {h}, {p.d_v}]")
+    _same_gpu((q_nope, q_rope, latent_cache, rope_cache, seqlens, W_UV, block_table, out),
+              ("q_nope", "q_rope", "latent_cache", "rope_cache", "seqlens", "W_UV", "block_table", "out"))
 
 
 def check_params(p: DecodeParams) -> None:
@@ -88,11 +155,7 @@ class Decoder:
         self.p = make_params(q_nope, q_rope, latent_cache, rope_cache, sm_scale=sm_scale, out_scale=out_scale,
                              max_seqlen=max_seqlen, page_size=page_size, max_pages_per_seq=maxp,
                              num_splits=num_splits)
-        for t, name in ((seqlens, "seqlens"), (block_table, "block_table")):
-            if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
-                raise ValueError(f"{name} must be a contiguous int32 tensor")
-        if W_UV.dtype != torch.float32 or not W_UV.is_contiguous():
-            raise ValueError("W_UV must be a contiguous float32 tensor [NB, h, DL, DV]")
+        _check_decode_tensors(self.p, q_nope, q_rope, latent_cache, rope_cache, seqlens, W_UV, block_table, out)
         dev = q_nope.device
         self.tensors = (q_nope, q_rope, latent_cache, rope_cache, block_table, seqlens, W_UV)
         self.out = out if out is not None else torch.empty(self.p.batch, self.p.num_heads, 128,
@@ -182,13 +245,21 @@ class Absorber:
     arguments are built once; each call is one launch."""
 
     def __init__(self, q_pre: torch.Tensor, W_UK: torch.Tensor, q_nope: torch.Tensor):
+        if q_nope.dim() != 4 or q_pre.dim() != 4 or W_UK.dim() != 4:
+            raise ValueError("q_pre must be [B, h, NB, d_nope], W_UK [NB, h, d_latent, d_nope], "
+                             "q_nope [B, h, NB, d_latent]")
         B, h, NB, DL = q_nope.shape
+        if q_pre.dtype not in _DTYPES or q_nope.dtype != q_pre.dtype:
+            raise ValueError("q_pre and q_nope must share one dtype (bfloat16 or float32)")
+        if tuple(W_UK.shape) != (NB, h, DL, q_pre.shape[3]):
+            raise ValueError(f"W_UK must be [{NB}, {h}, {DL}, {q_pre.shape[3]}] (got {list(W_UK.shape)})")
         if q_pre.shape[:3] != (B, h, NB) or q_pre.stride(3) != 1 or q_pre.dtype != q_nope.dtype:
             raise ValueError("q_pre must be [B, h, NB, d_nope] with contiguous rows and q_nope's dtype")
         if W_UK.dtype != torch.float32 or not W_UK.is_contiguous() or tuple(W_UK.shape[:3]) != (NB, h, DL):
             raise ValueError("W_UK must be a contiguous float32 tensor [NB, h, d_latent, d_nope]")
         if q_nope.stride(3) != 1 or q_nope.stride(2) != DL:
             raise ValueError("q_nope rows [NB, DL] must be contiguous")
+        _same_gpu((q_pre, W_UK, q_nope), ("q_pre", "W_UK", "q_nope"))
         p = DecodeParams()
         p.batch, p.num_heads, p.num_branches, p.d_latent, p.d_rope, p.d_v = B, h, NB, DL, 64, 128
         p.dtype = _DTYPES[q_nope.dtype]
@@ -217,8 +288,12 @@ def make_gqa_params(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
                     max_seqlen: int, page_size: int = 0, max_pages_per_seq: int = 0,
                     num_splits: int = 0) -> GqaParams:
     """q [B, H_q, 128], k_cache / v_cache [rows, H_kv, 128] (bf16; innermost rows contiguous)."""
+    if q.dim() != 3 or k_cache.dim() != 3 or v_cache.dim() != 3:
+        raise ValueError("q must be [B, H_q, 128], k_cache and v_cache [rows, H_kv, 128]")
     B, Hq, D = q.shape
     Hkv = k_cache.shape[1]
+    if k_cache.shape[2] != D or v_cache.shape[2] != D:
+        raise ValueError(f"k_cache and v_cache rows must hold {D} channels like q")
     if any(t.dtype != torch.bfloat16 for t in (q, k_cache, v_cache)):
         raise ValueError("q, k_cache and v_cache must be bfloat16")
     if q.stride(2) != 1 or k_cache.stride(2) != 1 or v_cache.stride(2) != 1 or v_cache.shape[1] != Hkv:
@@ -242,9 +317,12 @@ class GqaDecoder:
         maxp = 0 if block_table is None else block_table.shape[1]
         self.p = make_gqa_params(q, k_cache, v_cache, sm_scale=sm_scale, max_seqlen=max_seqlen,
                                  page_size=page_size, max_pages_per_seq=maxp, num_splits=num_splits)
-        for t, name in ((seqlens, "seqlens"), (block_table, "block_table")):
-            if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
-                raise ValueError(f"{name} must be a contiguous int32 tensor")
+        B = self.p.batch
+        if k_cache.dim() != 3 or v_cache.dim() != 3 or k_cache.shape[0] != v_cache.shape[0]:
+            raise ValueError("k_cache and v_cache must be [rows, H_kv, 128] with one row numbering")
+        _check_cache_rows(k_cache.shape[0], B, max_seqlen, page_size > 0, page_size, "k_cache")
+        _check_meta(seqlens, block_table, B, page_size > 0, max_seqlen, page_size)
+        _same_gpu((q, k_cache, v_cache, seqlens, block_table), ("q", "k_cache", "v_cache", "seqlens", "block_table"))
         check(lib().mlra_gqa_check_params(ctypes.byref(self.p)))
         self.tensors = (q, k_cache, v_cache, block_table, seqlens)
         self.out = torch.empty(q.shape[0], q.shape[1], q.shape[2], dtype=torch.float32, device=q.device)

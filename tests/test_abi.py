@@ -247,3 +247,124 @@ def test_absorb_argument_errors_before_any_launch():
     assert lib.mlra_absorb_query(fake, fake, fake, ctypes.byref(p), 128, i64(32 * 4 * 128), i64(4 * 128),
                                  i64(4), None) == -4                                          # 8-byte stride
     assert lib.mlra_absorb_query(fake, fake, fake, ctypes.byref(p), 128, i64(-1), *ok[1:], None) == -2
+
+
+# ----------------------------------------------------------------- binding: host-side tensor checks
+# Every mismatch below would send a kernel out of bounds if it reached the GPU. On this CPU-only
+# run the binding must refuse each one with its own message, before the device check (which a
+# fully consistent set of CPU tensors reaches last).
+
+def _cpu_inputs(paged=False, **kw):
+    from mlra_workloads import WORKLOADS, make_inputs
+    w = WORKLOADS[5 if paged else 2].replace(B=3, h=8, lengths=("list", (40, 1, 70)), **kw)
+    return w, make_inputs(w, seed=3)
+
+
+def _decoder(inp, w, **over):
+    import long_context_decode_mlra_amd as mlra
+    args = dict(q_nope=inp.q_nope, q_rope=inp.q_rope, latent_cache=inp.latent, rope_cache=inp.rope,
+                seqlens=inp.seqlens, W_UV=inp.W_UV, sm_scale=w.sm_scale, out_scale=w.gamma,
+                max_seqlen=inp.max_seqlen, block_table=inp.block_table, page_size=w.page_size, num_splits=4)
+    args.update(over)
+    qn, qr, lat, rp = args.pop("q_nope"), args.pop("q_rope"), args.pop("latent_cache"), args.pop("rope_cache")
+    return mlra.Decoder(qn, qr, lat, rp, **args)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_binding_consistent_cpu_tensors_reach_the_device_check(paged):
+    w, inp = _cpu_inputs(paged)
+    with pytest.raises(ValueError, match="must be GPU tensors"):
+        _decoder(inp, w)
+
+
+@pytest.mark.parametrize("case,match", [
+    ("seqlens_short", "seqlens must be"), ("seqlens_int64", "seqlens must be"),
+    ("q_rope_batch", "q_rope must be"), ("q_rope_heads", "q_rope must be"),
+    ("latent_rows", "needs B \\* max_seqlen"), ("rope_rows", "one row numbering"),
+    ("latent_heads", "latent_cache must be"), ("wuv_shape", "W_UV must be"), ("wuv_dtype", "W_UV must be"),
+    ("wuv_strided", "W_UV must be"), ("out_shape", "out must be"), ("out_dtype", "out must be"),
+    ("max_seqlen", "needs B \\* max_seqlen"), ("q_nope_3d", "q_nope must be"),
+])
+def test_binding_rejects_mismatched_tensors(case, match):
+    import torch
+    w, inp = _cpu_inputs()
+    B, h = 3, 8
+    over = {
+        "seqlens_short": dict(seqlens=inp.seqlens[:2]),
+        "seqlens_int64": dict(seqlens=inp.seqlens.long()),
+        "q_rope_batch": dict(q_rope=inp.q_rope[:2]),
+        "q_rope_heads": dict(q_rope=inp.q_rope[:, :4]),
+        "latent_rows": dict(latent_cache=inp.latent[:-1], rope_cache=inp.rope[:-1]),
+        "rope_rows": dict(rope_cache=inp.rope[:-1]),
+        "latent_heads": dict(latent_cache=inp.latent[:, :2]),
+        "wuv_shape": dict(W_UV=inp.W_UV[:, :4]),
+        "wuv_dtype": dict(W_UV=inp.W_UV.to(torch.bfloat16)),
+        "wuv_strided": dict(W_UV=inp.W_UV.transpose(2, 3)),
+        "out_shape": dict(out=torch.empty(B, h, 64)),
+        "out_dtype": dict(out=torch.empty(B, h, 128, dtype=torch.float64)),
+        "max_seqlen": dict(max_seqlen=inp.max_seqlen + 1),
+        "q_nope_3d": dict(q_nope=inp.q_nope.flatten(2)),
+    }[case]
+    with pytest.raises(ValueError, match=match):
+        _decoder(inp, w, **over)
+
+
+@pytest.mark.parametrize("case,match", [
+    ("no_table", "block_table must be"), ("table_rows", "block_table must be"),
+    ("table_cols", "fewer than max_seqlen"), ("table_int64", "block_table must be"),
+    ("pool_empty", "less than one page"),
+])
+def test_binding_rejects_mismatched_paged_tensors(case, match):
+    w, inp = _cpu_inputs(paged=True)
+    bt = inp.block_table
+    over = {
+        "no_table": dict(block_table=None),
+        "table_rows": dict(block_table=bt[:2]),
+        "table_cols": dict(block_table=bt[:, :1].contiguous(), max_seqlen=max(inp.max_seqlen, 2 * w.page_size)),
+        "table_int64": dict(block_table=bt.long()),
+        "pool_empty": dict(latent_cache=inp.latent[:1], rope_cache=inp.rope[:1]),
+    }[case]
+    with pytest.raises(ValueError, match=match):
+        _decoder(inp, w, **over)
+
+
+def test_binding_rejects_table_for_contiguous_cache():
+    w, inp = _cpu_inputs()
+    import torch
+    with pytest.raises(ValueError, match="page_size is 0"):
+        _decoder(inp, w, block_table=torch.zeros(3, 2, dtype=torch.int32))
+
+
+def test_gqa_binding_rejects_mismatched_tensors():
+    import torch
+    import long_context_decode_mlra_amd as mlra
+    from mlra_workloads import GQA_WORKLOADS, make_gqa_inputs
+    g = GQA_WORKLOADS["gqa_bf16_b32_hq64_hkv8_L32k"].replace(B=2, Hq=16, Hkv=2, lengths=("list", (33, 70)))
+    gi = make_gqa_inputs(g, seed=1)
+    kw = dict(sm_scale=g.sm_scale, max_seqlen=gi.max_seqlen, num_splits=4)
+    with pytest.raises(ValueError, match="must be GPU tensors"):
+        mlra.GqaDecoder(gi.q, gi.k_cache, gi.v_cache, seqlens=gi.seqlens, **kw)
+    with pytest.raises(ValueError, match="seqlens must be"):
+        mlra.GqaDecoder(gi.q, gi.k_cache, gi.v_cache, seqlens=gi.seqlens[:1], **kw)
+    with pytest.raises(ValueError, match="needs B \\* max_seqlen"):
+        mlra.GqaDecoder(gi.q, gi.k_cache[:-1], gi.v_cache[:-1], seqlens=gi.seqlens, **kw)
+    with pytest.raises(ValueError, match="one row numbering"):
+        mlra.GqaDecoder(gi.q, gi.k_cache, gi.v_cache[:-1], seqlens=gi.seqlens, **kw)
+    with pytest.raises(ValueError, match="128 channels"):
+        mlra.GqaDecoder(gi.q, gi.k_cache[..., :64], gi.v_cache[..., :64], seqlens=gi.seqlens, **kw)
+
+
+def test_absorber_rejects_mismatched_tensors():
+    import torch
+    import long_context_decode_mlra_amd as mlra
+    q_pre = torch.zeros(2, 8, 4, 128, dtype=torch.bfloat16)
+    W_UK = torch.zeros(4, 8, 128, 128)
+    q_nope = torch.zeros(2, 8, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="must be GPU tensors"):
+        mlra.Absorber(q_pre, W_UK, q_nope)
+    with pytest.raises(ValueError, match="W_UK must be"):
+        mlra.Absorber(q_pre, W_UK[:, :4], q_nope)
+    with pytest.raises(ValueError, match="share one dtype"):
+        mlra.Absorber(q_pre.float(), W_UK, q_nope)
+    with pytest.raises(ValueError, match="q_pre must be"):
+        mlra.Absorber(q_pre[:1], W_UK, q_nope)
