@@ -35,7 +35,8 @@
  *
  * Ownership: every array argument is a device pointer owned by the caller,
  * except `p` (host). No entry point allocates or frees memory; scratch
- * memory is the caller's `workspace`.
+ * memory is the caller's `workspace` (mlra_decode_noalloc: a fixed array of
+ * this library, one per device).
  *
  * Errors: 0 on success, a negative MLRA_ERR_* code otherwise, with a message
  * in mlra_last_error(). Contract on device data, not checked: 0 <= seqlens[b]
@@ -141,6 +142,26 @@ int mlra_decode_workspace_size(const mlra_decode_params* p, size_t* bytes);
 int mlra_decode(const void* q_nope, const void* q_rope, const void* latent_cache, const void* rope_cache,
                 const int32_t* block_table, const int32_t* seqlens, const float* W_UV, float* out,
                 const mlra_decode_params* p, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the fixed device array that is mlra_decode_noalloc's workspace (one per device). */
+#define MLRA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * mlra_decode without a caller workspace, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. The
+ * arguments and the result are those of mlra_decode; the workspace is a fixed array of
+ * MLRA_NOALLOC_SCRATCH_BYTES bytes inside this library, one per device, which the device
+ * holds from the first call until the process ends. The first call on a device looks its
+ * address up (hipGetSymbolAddress) with that device current; no call allocates or frees
+ * memory. A call whose mlra_decode_workspace_size exceeds MLRA_NOALLOC_SCRATCH_BYTES
+ * returns MLRA_ERR_WORKSPACE before touching the device. Every call on one device shares
+ * that device's array, and nothing in it needs to survive between calls (the kernels write
+ * what they later read), so calls that overlap on one device (two streams, two threads)
+ * race: serialise them, or give each its own workspace through mlra_decode.
+ */
+int mlra_decode_noalloc(const void* q_nope, const void* q_rope, const void* latent_cache, const void* rope_cache,
+                        const int32_t* block_table, const int32_t* seqlens, const float* W_UV, float* out,
+                        const mlra_decode_params* p, void* stream);
 
 /* First half of mlra_decode alone: the split-KV attention kernel, which leaves
  * per-split partials (unnormalised output, running max and sum per latent head

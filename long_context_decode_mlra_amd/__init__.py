@@ -13,13 +13,13 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (MLRA_BF16, MLRA_F32, MLRA_MAX_HEADS, MLRA_TILE_TOKENS, DecodeParams, GqaParams, MlraError,
-                   check, lib)
+from ._lib import (MLRA_BF16, MLRA_F32, MLRA_MAX_HEADS, MLRA_NOALLOC_SCRATCH_BYTES, MLRA_TILE_TOKENS, DecodeParams,
+                   GqaParams, MlraError, check, lib)
 
 __all__ = ["decode", "decode_splitkv", "decode_combine", "make_params", "Decoder", "workspace_size", "num_splits",
            "check_params", "plan", "copy_bandwidth_probe", "read_bandwidth_probe", "absorb_query", "Absorber", "MlraError",
            "DecodeParams", "GqaParams", "GqaDecoder", "gqa_decode", "make_gqa_params", "MLRA_BF16", "MLRA_F32",
-           "MLRA_TILE_TOKENS", "MLRA_MAX_HEADS", "lib"]
+           "MLRA_TILE_TOKENS", "MLRA_MAX_HEADS", "MLRA_NOALLOC_SCRATCH_BYTES", "lib"]
 
 _DTYPES = {torch.bfloat16: MLRA_BF16, torch.float32: MLRA_F32}
 

@@ -10,6 +10,7 @@ MLRA_BF16 = 0
 MLRA_F32 = 1
 MLRA_TILE_TOKENS = 32
 MLRA_MAX_HEADS = 64
+MLRA_NOALLOC_SCRATCH_BYTES = 64 << 20
 ABI_VERSION = 1
 
 ERRORS = {0: "MLRA_OK", -1: "MLRA_ERR_NULL", -2: "MLRA_ERR_SHAPE", -3: "MLRA_ERR_UNSUPPORTED",
@@ -17,7 +18,8 @@ ERRORS = {0: "MLRA_OK", -1: "MLRA_ERR_NULL", -2: "MLRA_ERR_SHAPE", -3: "MLRA_ERR
 
 # Every symbol include/mlra.h declares.
 EXPORTS = ("mlra_abi_version", "mlra_last_error", "mlra_check_params", "mlra_decode_num_splits",
-           "mlra_decode_workspace_size", "mlra_decode", "mlra_decode_splitkv", "mlra_decode_combine",
+           "mlra_decode_workspace_size", "mlra_decode", "mlra_decode_noalloc", "mlra_decode_splitkv",
+           "mlra_decode_combine",
            "mlra_decode_plan", "mlra_copy_bandwidth_probe", "mlra_read_bandwidth_probe", "mlra_absorb_query",
            "mlra_gqa_check_params", "mlra_gqa_num_splits", "mlra_gqa_workspace_size", "mlra_gqa_decode")
 
@@ -73,6 +75,7 @@ def lib() -> ctypes.CDLL:
     L.mlra_decode_num_splits.argtypes = [P, ctypes.POINTER(i32)]
     L.mlra_decode_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
     L.mlra_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, P, vp, sz, vp]
+    L.mlra_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, P, vp]
     L.mlra_decode_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, P, vp, sz, vp]
     L.mlra_decode_combine.argtypes = [vp, vp, vp, P, vp, sz, vp]
     L.mlra_decode_plan.argtypes = [vp, i32, i32, i32, vp, vp]

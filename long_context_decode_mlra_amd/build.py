@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 
 # HIP translation units of the library, compiled in parallel.
 HIP_SOURCES = ("mlra_attention.hip", "mlra_combine.hip", "mlra_absorb.hip", "mlra_probes.hip",
-               "gqa_attention.hip")
+               "gqa_attention.hip", "mlra_noalloc.hip")
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are kept out of every kernel.

@@ -368,3 +368,19 @@ def test_absorber_rejects_mismatched_tensors():
         mlra.Absorber(q_pre.float(), W_UK, q_nope)
     with pytest.raises(ValueError, match="q_pre must be"):
         mlra.Absorber(q_pre[:1], W_UK, q_nope)
+
+
+def test_noalloc_refuses_oversized_workspace_before_any_device_call():
+    """mlra_decode_noalloc checks the workspace its call needs against the fixed array first: with an
+    explicit split count that check needs no device, so it runs here."""
+    L = _lib()
+    lib = L.lib()
+    fake = ctypes.c_void_p(1 << 20)
+    p = good_params(num_splits=8, batch=20000, num_heads=64)
+    n = ctypes.c_size_t(0)
+    assert lib.mlra_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value > L.MLRA_NOALLOC_SCRATCH_BYTES
+    r = lib.mlra_decode_noalloc(fake, fake, fake, fake, None, fake, fake, fake, ctypes.byref(p), None)
+    assert r == -5
+    assert "mlra_decode_noalloc holds" in lib.mlra_last_error().decode()
+    assert lib.mlra_decode_noalloc(fake, fake, fake, fake, None, fake, fake, fake, None, None) == -1
