@@ -121,8 +121,8 @@ int mlra_decode_workspace_size(const mlra_decode_params* p, size_t* bytes);
 /*
  * Full decode step: split-KV attention (plan, tile stream, per-latent-head
  * online softmax, partials) followed by the combine: log-sum-exp merge of the
- * partials with the W_UV up-projection, then the branch sum and output scale.
- * Three kernel launches on `stream`.
+ * partials with the W_UV up-projection, the branch sum and the output scale in
+ * the same kernel. Two kernel launches on `stream`.
  *
  *   q_nope        [B][h] rows of NB*d_latent elements (strides q_stride_b/h); dtype
  *   q_rope        [B][h] rows of d_rope elements (strides qr_stride_b/h); dtype
@@ -170,10 +170,11 @@ int mlra_decode_splitkv(const void* q_nope, const void* q_rope, const void* late
                         const int32_t* block_table, const int32_t* seqlens, const mlra_decode_params* p,
                         void* workspace, size_t workspace_bytes, void* stream);
 
-/* Second half of mlra_decode alone (two launches): log-sum-exp merge of the
+/* Second half of mlra_decode alone (one launch): log-sum-exp merge of the
  * partials that mlra_decode_splitkv left in `workspace` (same p, same seqlens,
  * same workspace, after it on the same stream), then
- * out[b,i] = out_scale * sum_j obar_j @ W_UV[j,i]. */
+ * out[b,i] = out_scale * sum_j obar_j @ W_UV[j,i]. It may run again on the same
+ * partials (it leaves the workspace as it found it). */
 int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, float* out, const mlra_decode_params* p,
                         void* workspace, size_t workspace_bytes, void* stream);
 

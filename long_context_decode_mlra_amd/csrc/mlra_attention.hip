@@ -100,12 +100,24 @@ struct DecodeArgs {
   float* part_o;
   float* part_ml;
   int64_t* prefix;  // [B + 3]: first global tile of each sequence, then T, T, G (written by workgroup 0)
+  int* counters;    // [n_counters]: the combine kernel's arrival counters, cleared here
+  int n_counters;
   int B, h, G_req, page_size, max_seqlen, max_pages;
   int G_small;                       // > 0: use this many splits when splits would be short (see split_plan)
   int64_t q_sb, q_sh, qr_sb, qr_sh;  // bytes
   int64_t lat_stride, rope_stride;   // bytes
   float c;                           // sm_scale * log2(e)
 };
+
+// Clears this workgroup's share of the arrival counters that the combine kernel after it on the
+// stream counts its workgroups in (every launched workgroup takes an equal slice; the kernel
+// boundary makes the zeros visible to the combine).
+__device__ __forceinline__ void clear_counters(const DecodeArgs& a) {
+  const int per = (a.n_counters + int(gridDim.x) - 1) / int(gridDim.x);
+  const int lo = int(blockIdx.x) * per;
+  const int hi = min(a.n_counters, lo + per);
+  for (int k = lo + int(threadIdx.x); k < hi; k += int(blockDim.x)) a.counters[k] = 0;
+}
 
 // The split plan of a launch of G_req workgroups, switched to G_small splits when the tiles
 // would give fewer than kMinTilesPerSplit per split. Workgroups g >= G exit at once; the first
@@ -418,6 +430,7 @@ void decode_kernel(DecodeArgs a) {
   const int head = hb * kHeadBlock + n;
   const bool head_ok = head < a.h;
 
+  clear_counters(a);
   const Lens lens = load_lens(a.seqlens, a.B);
   const Plan plan = split_plan(a, lens);
   if (blockIdx.x == 0 && wave == 0) write_prefix(lens, plan, a.prefix);
@@ -876,6 +889,7 @@ void decode_branch_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < kBrLoads; ++i) full[i] = br_load_offset(a, i, j, lane, kTile - 1);
 
+  clear_counters(a);
   const Lens lens = load_lens(a.seqlens, a.B);
   const Plan plan = split_plan(a, lens);
   if (blockIdx.x == 0 && j == 0) write_prefix(lens, plan, a.prefix);
@@ -901,6 +915,7 @@ void decode_shard_kernel(DecodeArgs a) {
 #pragma unroll
   for (int i = 0; i < kBrLoads; ++i) full[i] = br_load_offset(a, i, 0, lane, kTile - 1);
 
+  clear_counters(a);
   const Lens lens = load_lens(a.seqlens, a.B);
   const Plan plan = split_plan(a, lens);
   if (blockIdx.x == 0 && wave == 0) write_prefix(lens, plan, a.prefix);
@@ -949,6 +964,7 @@ void decode_hs_kernel(DecodeArgs a) {
   const int head = 16 * hq + n16;
   const bool head_ok = head < a.h;
 
+  clear_counters(a);
   const Lens lens = load_lens(a.seqlens, a.B);
   const Plan plan = split_plan(a, lens);
   if (blockIdx.x == 0 && wave == 0) write_prefix(lens, plan, a.prefix);
@@ -1236,6 +1252,8 @@ extern "C" int mlra_decode_splitkv(const void* q_nope, const void* q_rope, const
   a.part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + lay.part_o_off);
   a.part_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + lay.part_ml_off);
   a.prefix = reinterpret_cast<int64_t*>(static_cast<unsigned char*>(workspace) + lay.prefix_off);
+  a.counters = reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + lay.counters_off);
+  a.n_counters = int(lay.n_counters);
   a.B = p->batch;
   a.h = p->num_heads;
   a.G_req = G;

@@ -16,7 +16,7 @@ namespace {
 // ------------------------------------------------------------------ combine kernel
 //
 // One workgroup per (query head i, block q of kCombBlock of the NB * d_latent latent channels
-// (512, or 128 in the shard form), run of `sub` sequences). Block q lies in latent head j =
+// (512, or 128 in the shard form), run z of `sub` sequences). Block q lies in latent head j =
 // q*kCombBlock / d_latent, channels c0..c0+kCombBlock-1 of it, c0 = q*kCombBlock % d_latent.
 // The runs tile the 32-sequence groups of the ypart layout (sub is 32, 16, 8 or 4).
 //  1. merge:   obar[b][k] = sum_s 2^{m_s-M} O_s[c0+k] / sum_s 2^{m_s-M} l_s over the splits
@@ -24,10 +24,14 @@ namespace {
 //  2. project: y_q[b][d] = sum_k obar[b][k] * W_UV[j][i][c0+k][d] on fp32 MFMA
 //              (M = sequences, N = 128 output channels, K = kCombBlock). Every W_UV row is
 //              read by exactly one workgroup of the grid.
-//  y_q goes to the workspace; finalize_kernel adds the blocks in the fixed order q = 0, 1, ...
-//  (the branch sum) and applies out_scale. (Summing inside this kernel would need
-//  device-scope fences between workgroups on different L2 slices; their write-back and
-//  invalidate cost more than the extra launch.)
+//  3. branch sum: y_q goes to the workspace with stores that reach the device's coherence
+//              point (sc1), and once they are complete the workgroup counts itself in the
+//              arrival counter of (i, z). The last of the head's NBLK block workgroups to arrive
+//              reads every y_q' of the run back (sc1 loads, which do not hit a stale L2 line of
+//              its own XCD), adds them in the fixed order q' = 0, 1, ..., applies out_scale and
+//              stores out, then resets the counter. The sum is the same whichever workgroup
+//              arrives last. No workgroup waits for another. (Fences at device scope would
+//              write back and invalidate the XCD's whole L2 instead of these few lines.)
 
 struct CombineArgs {
   const float* part_o;
@@ -35,13 +39,16 @@ struct CombineArgs {
   const int64_t* prefix;
   const float* W_UV;
   float* ypart;    // [groups][h][nblk][32][128]
+  int* counters;   // [h][runs]: arrivals per (query head, run); zero before the launch
+  float* out;      // [B][h][128]
   int B, h;
-  int nblk;        // kCombBlock-channel blocks of the NB * d_latent latent channels
   int sub;         // sequences per workgroup: a power of two dividing kCombSeqs
+  float out_scale;
 };
 
 constexpr int kCombSeqs = 32;
 constexpr int kCombTPS = kCombBlock / 16;  // merge threads per sequence, 4 channel quads each
+constexpr int kSc1 = 16;                   // cache-policy bits of the buffer builtins: sc1
 
 struct MergeState {
   float M, den;
@@ -67,12 +74,20 @@ __device__ __forceinline__ void merge_in(MergeState& st, float m, float l, const
 // Workgroup barrier that orders LDS only (the W_UV loads issued first stay in flight).
 __device__ __forceinline__ void comb_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// Buffer resource over `bytes` bytes at p (raw buffer, range-checked: reads past it return 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t comb_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), short(0), bytes, 0x00020000);
+}
+
 template <int NB, int DL>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int kBatch = 4;  // slots loaded together
   constexpr int kSteps = kCombBlock / 2;  // K steps of the 32x32x2 MFMA
+  constexpr int NBLK = NB * DL / kCombBlock;
+  constexpr int kBlockFloats = kCombSeqs * kDV;
   __shared__ float ob[kCombBlock][kCombSeqs];  // merged block, k-major: ob[k][b]
   __shared__ float st_red[18 * 128];            // per (receiving slot part, pair): M, den, acc[16]
+  __shared__ int last_arrival;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -86,16 +101,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int c0 = (q * kCombBlock) % DL;
   const int nb = min(a.sub, a.B - b0);
   const int n = lane & 31, hh = lane >> 5;
-
-  // The W_UV slice this wave multiplies by (rows c0 + 2kb + hh, column 32*wave + n), issued
-  // first so that the loads overlap the merge.
-  const float* wcol = a.W_UV + ((int64_t(j) * a.h + i) * DL + c0) * kDV + 32 * wave + n;
-  float wv[kSteps];
-#pragma unroll
-  for (int kb = 0; kb < kSteps; ++kb) wv[kb] = wcol[(2 * kb + hh) * kDV];
-  __builtin_amdgcn_sched_barrier(0);
-
-  const Plan plan{a.prefix[a.B + 1], int(a.prefix[a.B + 2])};
 
   // ---- 1. merge. kCombTPS threads per sequence, each owning channel quads cq0 + kCombTPS*v
   // (v < 4); with nbp = nb rounded up to a power of two, S = 256 / (nbp * kCombTPS) slot
@@ -111,32 +116,53 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const bool live = bl < nb;
   const int b = b0 + (live ? bl : 0);
 
+  // The sequence's first and end tiles, then its first batch of partials, then the W_UV slice
+  // this wave multiplies by (rows c0 + 2kb + hh, column 32*wave + n). Vector loads retire in
+  // order, so the W_UV loads go out after the first partials, which the merge waits for while
+  // W_UV is still on its way.
+  const int64_t P0 = a.prefix[b], P1 = a.prefix[b + 1];
+  const Plan plan{a.prefix[a.B + 1], int(a.prefix[a.B + 2])};
+  // Splits gf..gl hold the tiles of sequence b (none when it is empty or the thread idle).
+  int64_t gf = 0, gl = -1;
+  if (live && P1 > P0) {
+    gf = split_of_tile(P0, plan);
+    gl = split_of_tile(P1 - 1, plan);
+  }
+  // Slots g, g + S, ... of the sequence; past the last one the last is read again (slot 0 of
+  // the head when there is none) and skipped through m = -inf.
+  floatx2 ml[kBatch];
+  floatx4 o[kBatch][4];
+  auto load_batch = [&](int64_t g) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t gg = g + int64_t(u) * S;
+      const int64_t slot = gl >= 0 ? min(gg, gl) + b : 0;
+      const int64_t row = (slot * NB + j) * a.h + i;
+      ml[u] = *reinterpret_cast<const floatx2*>(a.part_ml + row * 2);
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        o[u][v] = *reinterpret_cast<const floatx4*>(a.part_o + row * DL + c0 + 4 * (cq0 + kCombTPS * v));
+      if (gg > gl) ml[u][0] = -INFINITY;
+    }
+  };
+  load_batch(gf + r);
+  const float* wcol = a.W_UV + ((int64_t(j) * a.h + i) * DL + c0) * kDV + 32 * wave + n;
+  float wv[kSteps];
+#pragma unroll
+  for (int kb = 0; kb < kSteps; ++kb) wv[kb] = wcol[(2 * kb + hh) * kDV];
+  __builtin_amdgcn_sched_barrier(0);
+
   MergeState st;
   st.M = -INFINITY;
   st.den = 0.f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) st.acc[u] = floatx4{};
-  if (live) {
-    const int64_t P0 = a.prefix[b], P1 = a.prefix[b + 1];
-    if (P1 > P0) {
-      const int64_t gf = split_of_tile(P0, plan), gl = split_of_tile(P1 - 1, plan);
-      for (int64_t g = gf + r; g <= gl; g += kBatch * S) {
-        floatx2 ml[kBatch];
-        floatx4 o[kBatch][4];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int64_t gg = g + int64_t(u) * S;
-          const int64_t row = ((min(gg, gl) + b) * NB + j) * a.h + i;
-          ml[u] = *reinterpret_cast<const floatx2*>(a.part_ml + row * 2);
+  for (int u = 0; u < kBatch; ++u) merge_in(st, ml[u][0], ml[u][1], o[u]);
+  for (int64_t g = gf + r + kBatch * S; g <= gl; g += kBatch * S) {
+    load_batch(g);
 #pragma unroll
-          for (int v = 0; v < 4; ++v)
-            o[u][v] = *reinterpret_cast<const floatx4*>(a.part_o + row * DL + c0 + 4 * (cq0 + kCombTPS * v));
-          if (gg > gl) ml[u][0] = -INFINITY;  // past the end: re-read the last slot, then skip it
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) merge_in(st, ml[u][0], ml[u][1], o[u]);
-      }
-    }
+    for (int u = 0; u < kBatch; ++u) merge_in(st, ml[u][0], ml[u][1], o[u]);
   }
   if (S > 1) {
     // Tree over the slot parts in a fixed order: at each level, part r + half hands its state
@@ -181,45 +207,46 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   }
   __syncthreads();
 
-  // ---- 2. project: wave w computes output channels [32w, 32w+32) for the group's 32 rows;
-  // the rows of this run are stored.
+  // ---- 2. project: wave w computes output channels [32w, 32w+32) for the group's 32 rows.
   floatx16 y = {};
 #pragma unroll
   for (int kb = 0; kb < kSteps; ++kb) y = __builtin_amdgcn_mfma_f32_32x32x2f32(ob[2 * kb + hh][n], wv[kb], y, 0, 0, 0);
 
-  float* yq = a.ypart + ((int64_t(grp) * a.h + i) * a.nblk + q) * (kCombSeqs * kDV);
+  // ---- 3. hand y_q over (rows of this run only) and count the arrival.
+  float* yhead = a.ypart + (int64_t(grp) * a.h + i) * NBLK * kBlockFloats;
+  float* yq = yhead + q * kBlockFloats;
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
     const int row = 8 * (rr >> 2) + 4 * hh + (rr & 3);
-    if (unsigned(row - s0) < unsigned(nb)) yq[row * kDV + 32 * wave + n] = y[rr];
+    if (unsigned(row - s0) < unsigned(nb))
+      __hip_atomic_store(yq + row * kDV + 32 * wave + n, y[rr], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-}
+  // Every store of the workgroup has reached the coherence point before the count.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int* counter = a.counters + int64_t(i) * gridDim.z + blockIdx.z;
+  if (tid == 0)
+    last_arrival = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == NBLK - 1;
+  __syncthreads();
+  if (!last_arrival) return;
 
-// out[b][i][:] = out_scale * (y_0 + y_1 + ...)[b][:], blocks added in this order.
-struct FinalizeArgs {
-  const float* ypart;
-  float* out;
-  int B, h;
-  float out_scale;
-};
-
-template <int NBLK>
-__global__ __launch_bounds__(256) void finalize_kernel(FinalizeArgs a) {
-  const int64_t n4 = int64_t(a.B) * a.h * (kDV / 4);
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (idx >= n4) return;
-  const int d4 = int(idx % (kDV / 4));
-  const int64_t bi = idx / (kDV / 4);
-  const int i = int(bi % a.h);
-  const int b = int(bi / a.h);
-  const int grp = b / kCombSeqs, bl = b % kCombSeqs;
-  const floatx4* y = reinterpret_cast<const floatx4*>(
-                         a.ypart + ((int64_t(grp) * a.h + i) * NBLK) * (kCombSeqs * kDV) + bl * kDV) + d4;
-  constexpr int kBlk = kCombSeqs * kDV / 4;
-  floatx4 v = y[0];
+  // ---- 4. the last arrival: out[b0 + t][i][:] = out_scale * (y_0 + y_1 + ...)[s0 + t][:].
+  const __amdgpu_buffer_rsrc_t yr = comb_rsrc(yhead, NBLK * kBlockFloats * int(sizeof(float)));
+  constexpr int kQuads = kDV / 4;
+  for (int idx = tid; idx < nb * kQuads; idx += 256) {
+    const int t = idx / kQuads, d4 = idx % kQuads;
+    const int off = ((s0 + t) * kDV + 4 * d4) * int(sizeof(float));
+    floatx4 v[NBLK];
 #pragma unroll
-  for (int qq = 1; qq < NBLK; ++qq) v += y[qq * kBlk];
-  reinterpret_cast<floatx4*>(a.out)[idx] = a.out_scale * v;
+    for (int qq = 0; qq < NBLK; ++qq)
+      v[qq] = __builtin_amdgcn_raw_buffer_load_b128(yr, off + qq * kBlockFloats * int(sizeof(float)), 0, kSc1);
+    floatx4 sum = v[0];
+#pragma unroll
+    for (int qq = 1; qq < NBLK; ++qq) sum += v[qq];
+    *reinterpret_cast<floatx4*>(a.out + (int64_t(b0 + t) * a.h + i) * kDV + 4 * d4) = a.out_scale * sum;
+  }
+  // Ready for a later combine on the same workspace (the attention kernel clears it as well).
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Sequences per combine workgroup: 32 (or B rounded up to a power of two, at least 4),
@@ -259,17 +286,11 @@ int device_cus(int* cus) {
 }
 
 using CombineFn = void (*)(CombineArgs);
-using FinalizeFn = void (*)(FinalizeArgs);
 
 CombineFn pick_combine(int nb, int dl) {
   if (nb == 4) return combine_kernel<4, 128>;
   if (nb == 2) return combine_kernel<2, 256>;
   return dl == kShardLatent ? combine_kernel<1, kShardLatent> : combine_kernel<1, 512>;
-}
-
-FinalizeFn pick_finalize(int nblk) {
-  return nblk == kShardLatent / kCombBlock ? finalize_kernel<kShardLatent / kCombBlock>
-                                           : finalize_kernel<kLatentTotal / kCombBlock>;
 }
 
 }  // namespace
@@ -295,29 +316,21 @@ extern "C" int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, fl
   c.prefix = reinterpret_cast<const int64_t*>(ws + lay.prefix_off);
   c.W_UV = W_UV;
   c.ypart = reinterpret_cast<float*>(ws + lay.ypart_off);
+  c.counters = reinterpret_cast<int*>(ws + lay.counters_off);
+  c.out = out;
   c.B = p->batch;
   c.h = p->num_heads;
-  c.nblk = latent_total(*p) / kCombBlock;
+  c.out_scale = p->out_scale;
+  const int nblk = latent_total(*p) / kCombBlock;
   int cus = 0;
   rc = device_cus(&cus);
   if (rc) return rc;
-  c.sub = combine_sub(p->batch, p->num_heads, c.nblk, cus);
-  const dim3 grid(p->num_heads, c.nblk, (p->batch + c.sub - 1) / c.sub);
+  c.sub = combine_sub(p->batch, p->num_heads, nblk, cus);
+  const dim3 grid(p->num_heads, nblk, (p->batch + c.sub - 1) / c.sub);
   hipLaunchKernelGGL(pick_combine(p->num_branches, p->d_latent), grid, dim3(256), 0,
                      static_cast<hipStream_t>(stream), c);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");
-  FinalizeArgs f;
-  f.ypart = c.ypart;
-  f.out = out;
-  f.B = p->batch;
-  f.h = p->num_heads;
-  f.out_scale = p->out_scale;
-  const int64_t n4 = int64_t(p->batch) * p->num_heads * (kDV / 4);
-  hipLaunchKernelGGL(pick_finalize(c.nblk), dim3(unsigned((n4 + 255) / 256)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), f);
-  e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "finalize kernel launch");
   return MLRA_OK;
 }
 

@@ -33,6 +33,8 @@ inline bool is_shard(const mlra_decode_params& p) { return p.num_branches == 1 &
 //   prefix  int64 [B + 3]                  first tile of each sequence, then T (total tiles), T, G
 //   ypart   fp32 [groups][h][NB*d_latent/kCombBlock][32][d_v]  projected channel blocks of up to
 //                                          32 sequences
+//   counters int32 [h][ceil(B / kCombMinSub)]  arrivals of the combine workgroups of one (query
+//                                          head, run of sequences); the attention kernel clears them
 // groups = ceil(B / 32).
 struct WorkspaceLayout {
   int64_t slots = 0;
@@ -40,8 +42,13 @@ struct WorkspaceLayout {
   size_t part_ml_off = 0;
   size_t prefix_off = 0;
   size_t ypart_off = 0;
+  size_t counters_off = 0;
+  int64_t n_counters = 0;
   size_t total = 0;
 };
+
+// Fewest sequences one combine workgroup takes (its runs hold 32, 16, 8 or 4 sequences).
+constexpr int kCombMinSub = 4;
 
 WorkspaceLayout workspace_layout(const mlra_decode_params& p, int32_t num_splits);
 

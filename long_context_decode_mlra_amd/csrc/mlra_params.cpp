@@ -1,5 +1,6 @@
 // Host-only part of the C ABI: parameter validation, workspace sizing, error text.
 // No HIP calls here, so every error path can be driven from a machine without a GPU.
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -37,8 +38,10 @@ WorkspaceLayout workspace_layout(const mlra_decode_params& p, int32_t num_splits
   w.prefix_off = align256(w.part_ml_off + size_t(w.slots) * per_slot_ml);
   const size_t groups = (size_t(p.batch) + 31) / 32;
   w.ypart_off = align256(w.prefix_off + (size_t(p.batch) + 3) * sizeof(int64_t));
-  w.total = align256(w.ypart_off + groups * size_t(p.num_heads) * (latent_total(p) / kCombBlock) * 32 * kDV *
-                                       sizeof(float));
+  w.counters_off = align256(w.ypart_off + groups * size_t(p.num_heads) * (latent_total(p) / kCombBlock) * 32 *
+                                              kDV * sizeof(float));
+  w.n_counters = int64_t(p.num_heads) * ((int64_t(p.batch) + kCombMinSub - 1) / kCombMinSub);
+  w.total = align256(w.counters_off + size_t(w.n_counters) * sizeof(int32_t));
   return w;
 }
 
@@ -52,6 +55,9 @@ int prepare(const mlra_decode_params* p, const int32_t* seqlens, void* workspace
   rc = mlra_decode_num_splits(p, G);
   if (rc) return rc;
   *lay = workspace_layout(*p, *G);
+  if (lay->n_counters > INT32_MAX)
+    return set_error(MLRA_ERR_SHAPE, "batch %d with %d heads is past what the combine counts", p->batch,
+                     p->num_heads);
   if (p->batch == 0) return MLRA_OK;
   if (!seqlens) return set_error(MLRA_ERR_NULL, "seqlens is NULL");
   if (!workspace) return set_error(MLRA_ERR_WORKSPACE, "workspace is NULL");

@@ -53,6 +53,8 @@ def assert_parity(got, ref, max_abs=MAX_ABS, rel_l2=REL_L2, label=""):
 SMALL = {
     "mlra4_bf16": WORKLOADS[2],
     "mla_bf16": WORKLOADS[4],
+    # MLA at the scale of its own 576-channel logit (the workloads use 1/sqrt(192) for both forms)
+    "mla_bf16_scale576": WORKLOADS[4].replace(sm_scale=1.0 / math.sqrt(576.0)),
     "mlra2_bf16": WORKLOADS[2].replace(name="mlra2", NB=2, DL=256, rope_std=1.0),
     "mlra4_f32": WORKLOADS[1].replace(h=32),
     "mla_f32": WORKLOADS[4].replace(dtype="f32"),
@@ -264,13 +266,14 @@ def test_four_shards_sum_to_mlra4():
 
 
 # ----------------------------------------------------------------- full-size workloads, sampled sequences
-FULL = {2: (0, 17, 31), 3: (0, 1, 2, 3), 4: (0, 31), 5: (0, 13, 40, 63), 6: (0, 31), 7: (0, 31)}
+FULL = {2: tuple(range(32)), 3: (0, 1, 2, 3), 4: (0, 31), 5: (0, 13, 40, 63), 6: (0, 31), 7: (0, 31)}
 
 
 @pytest.mark.parametrize("cfg", sorted(FULL))
 def test_full_size_sampled(cfg):
     """The workload at its full size in the launch configuration the benchmark times
-    (num_splits = one per resident slot); the oracle checks sampled sequences."""
+    (num_splits = one per resident slot); the oracle checks sampled sequences (every sequence
+    of the B=32, L=32K MLRA-4 workload)."""
     w = WORKLOADS[cfg]
     inp = make_inputs(w, seed=cfg)
     print(f"cfg{cfg}: B={w.B} tokens={inp.total_tokens} max_seqlen={inp.max_seqlen}", flush=True)
@@ -279,6 +282,17 @@ def test_full_size_sampled(cfg):
     ref = oracle.decode_inputs(inp, batch_indices=sel)
     assert np.all(np.isfinite(got))
     assert_parity(got[list(sel)], ref, label=f"cfg{cfg} sampled {sel}")
+
+
+def test_mla_full_size_scale_576():
+    """Absorbed MLA at its full size with the softmax scale of a 576-channel logit, 1/sqrt(576)."""
+    w = WORKLOADS[4].replace(sm_scale=1.0 / math.sqrt(576.0))
+    inp = make_inputs(w, seed=4)
+    got = gpu_decode(inp, 0)
+    sel = (0, 9, 31)
+    ref = oracle.decode_inputs(inp, batch_indices=sel)
+    assert np.all(np.isfinite(got))
+    assert_parity(got[list(sel)], ref, label=f"cfg4 scale 1/sqrt(576) sampled {sel}")
 
 
 def test_two_sequence_groups_and_workspace_reuse():
@@ -362,6 +376,26 @@ def test_graph_replay_matches_eager(cfg):
         torch.cuda.synchronize()
     assert_parity(eager.cpu().double().numpy(), oracle.decode_inputs(inp), label=f"graph cfg{cfg}")
 
+
+@pytest.mark.parametrize("cfg", [2, 7, 4])
+def test_combine_reruns_on_the_same_partials(cfg):
+    """The combine counts its workgroups per (query head, run of sequences) and the last one of a
+    head adds the branch blocks: after one attention launch, three combine launches in a row each
+    give the full decode's bits (the counters are back at zero after every combine)."""
+    mlra = _mlra()
+    w = WORKLOADS[cfg].replace(B=37, lengths=("list", tuple(range(1, 37 * 53, 53))))
+    inp = make_inputs(w, seed=70 + cfg)
+    d = inp.to("cuda")
+    dec = mlra.Decoder(d.q_nope, d.q_rope, d.latent, d.rope, seqlens=d.seqlens, W_UV=d.W_UV, sm_scale=w.sm_scale,
+                       out_scale=w.gamma, max_seqlen=inp.max_seqlen)
+    full = dec().clone()
+    dec.splitkv()
+    for k in range(3):
+        dec.out.fill_(float("nan"))
+        dec.combine()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.out, full), f"combine run {k}"
+    assert_parity(full.cpu().double().numpy(), oracle.decode_inputs(inp), label=f"rerun cfg{cfg}")
 
 def test_two_streams_two_workspaces():
     """Two decodes with their own workspaces, enqueued on two streams (default priority) so that
