@@ -81,6 +81,17 @@ def attention_kernel_name(w):
     return "decode_kernel"
 
 
+def attention_kernel_design(w):
+    """One line on how the attention kernel of this workload is organised."""
+    return {
+        "decode_branch_kernel": "one barrier-free wave per latent head, private LDS rings, one workgroup per CU",
+        "decode_shard_kernel": "one barrier-free wave per split of the one latent head, private LDS rings",
+        "decode_hs_kernel": "split-head: wave pairs over 256 latent channels each, whole tiles shared, one "
+                            "LDS-only barrier per tile, two workgroups per CU (not MLRA-4's design)",
+        "decode_kernel": "whole tiles shared by the workgroup, one LDS-only barrier per tile",
+    }[attention_kernel_name(w)]
+
+
 def algorithmic_bytes(inp):
     """Bytes the method must move once per step: cache rows of every cached token,
     queries, W_UV, the output, plus the int32 metadata."""
@@ -476,6 +487,7 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": (trec["hbm_bytes_per_launch"] if trec else None),
                 "kernel": attention_kernel_name(w) + " (split-KV attention)",
+                "attention_kernel_design": attention_kernel_design(w),
                 "algorithmic_bytes_per_launch": ab["attention"],
                 "avg_launch_us": round(dk_mean * 1e3, 2),
                 "timing": "HIP events on the launch stream around each attention launch of K settled steps"}
