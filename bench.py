@@ -214,7 +214,7 @@ def record_mfma(counter_csv, args):
             continue
         acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
         spans[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
-        kname = k.split("(")[0]
+        kname = re.search(r"decode_\w*kernel(<[^>]*>)?", k).group(0)
     mean = {c: sum(v) / len(v) for c, v in acc.items()}
     w = WORKLOADS[args.config]
     inp = make_inputs(w, seed=args.config)
