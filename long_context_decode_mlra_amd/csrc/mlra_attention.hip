@@ -97,7 +97,8 @@ struct DecodeArgs {
   const unsigned char* rope;
   const int32_t* block_table;
   const int32_t* seqlens;
-  float* part_o;
+  void* part_o;     // fp32 (fp32 caches) or fp16 with per-64-channel-block exponents (bf16 caches)
+  int* part_e;      // those exponents (bf16 caches)
   float* part_ml;
   int64_t* prefix;  // [B + 3]: first global tile of each sequence, then T, T, G (written by workgroup 0)
   int* counters;    // [n_counters]: the combine kernel's arrival counters, cleared here
@@ -126,6 +127,56 @@ __device__ __forceinline__ Plan split_plan(const DecodeArgs& a, const Lens& lens
   Plan p = make_plan(lens, a.G_req);
   if (a.G_small > 0 && p.T < int64_t(kMinTilesPerSplit) * a.G_req) p.G = int(p.T < a.G_small ? p.T : a.G_small);
   return p;
+}
+
+// ---- partials of bf16 caches: fp16 values, one exponent e per 64-channel block, the block
+// stored as x * 2^-e. With e taken so that the block's largest magnitude is below 2^(e + 15), no
+// stored value can overflow, whatever the cache holds, and each keeps 11 significant bits
+// relative to its block's largest value (rounded to nearest even). Halving the partials
+// halves the bytes the attention kernel writes at its end and the combine reads.
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ int part_exp(float mx) { return __builtin_amdgcn_frexp_expf(mx) - 15; }
+
+__device__ __forceinline__ halfx8 half8_scaled(const float* v, int e) {
+  halfx8 h;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) h[k] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(v[k], -e));
+  return h;
+}
+
+// The two block exponents of a 128-channel slice held as in tile_pv (lane (n, hh) holds channel
+// 32*gg + 16*hh + 4*i + mb in O[mb][4*gg + i]; gg < 2 is block 0). Every lane of the wave calls
+// it: a block's largest magnitude combines both lane halves.
+__device__ __forceinline__ void slice_exps(const floatx16 (&O)[4], int (&e)[2]) {
+  float mx[2] = {0.f, 0.f};
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) mx[gg >> 1] = fmaxf(mx[gg >> 1], fabsf(O[mb][4 * gg + i]));
+#pragma unroll
+  for (int k = 0; k < 2; ++k) e[k] = part_exp(fmaxf(mx[k], __shfl_xor(mx[k], 32, 64)));
+}
+
+// Store the slice (dst: its first channel; dst_e: its first block's exponent).
+__device__ __forceinline__ void store_slice_f16(_Float16* dst, int* dst_e, const floatx16 (&O)[4], int hh,
+                                                const int (&e)[2]) {
+#pragma unroll
+  for (int gg = 0; gg < 4; ++gg) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) v[4 * i + mb] = O[mb][4 * gg + i];
+    *reinterpret_cast<halfx8*>(dst + 32 * gg + 16 * hh) = half8_scaled(v, e[gg >> 1]);
+    *reinterpret_cast<halfx8*>(dst + 32 * gg + 16 * hh + 8) = half8_scaled(v + 8, e[gg >> 1]);
+  }
+  if (hh == 0) {
+    dst_e[0] = e[0];
+    dst_e[1] = e[1];
+  }
 }
 
 // Split run by workgroup wg of the n active ones. Workgroups are dealt round-robin over the
@@ -548,14 +599,22 @@ void decode_kernel(DecodeArgs a) {
     // Partial of split g for sequence b, slot g + b.
     const int64_t pslot = int64_t(g) + b;
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    [[maybe_unused]] int e[2];
+    if constexpr (sizeof(T) == 2) slice_exps(O, e);
     if (head_ok) {
-      float* dst = a.part_o + ((pslot * NB + j) * a.h + head) * G::kDL + sub * 128;
+      const int64_t row = (pslot * NB + j) * a.h + head;
+      if constexpr (sizeof(T) == 2) {
+        store_slice_f16(static_cast<_Float16*>(a.part_o) + row * G::kDL + sub * 128,
+                        a.part_e + row * (G::kDL / kPartBlock) + 2 * sub, O, hh, e);
+      } else {
+        float* dst = static_cast<float*>(a.part_o) + row * G::kDL + sub * 128;
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg)
+        for (int gg = 0; gg < 4; ++gg)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<floatx4*>(dst + 32 * gg + 16 * hh + 4 * i) =
-              floatx4{O[0][4 * gg + i], O[1][4 * gg + i], O[2][4 * gg + i], O[3][4 * gg + i]};
+          for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<floatx4*>(dst + 32 * gg + 16 * hh + 4 * i) =
+                floatx4{O[0][4 * gg + i], O[1][4 * gg + i], O[2][4 * gg + i], O[3][4 * gg + i]};
+      }
       if (hh == 0 && sub == 0) {
         float* ml = a.part_ml + ((pslot * NB + j) * a.h + head) * 2;
         ml[0] = m_run;
@@ -811,19 +870,18 @@ __device__ __forceinline__ void br_segment(const DecodeArgs& a, int b, int L, in
   }
 }
 
-// The partial of latent head j (of NB) at slot pslot.
+// The partial of latent head j (of NB) at slot pslot. Called by every lane of the wave; lanes of
+// heads past h store nothing.
 template <int NB>
 __device__ __forceinline__ void br_store_partial(const DecodeArgs& a, int64_t pslot, int j, int n, int hh,
-                                                 const BrAcc& acc, float l_tot) {
-  float* dst = a.part_o + ((pslot * NB + j) * a.h + n) * 128;
-#pragma unroll
-  for (int gg = 0; gg < 4; ++gg)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<floatx4*>(dst + 32 * gg + 16 * hh + 4 * i) =
-          floatx4{acc.O[0][4 * gg + i], acc.O[1][4 * gg + i], acc.O[2][4 * gg + i], acc.O[3][4 * gg + i]};
+                                                 bool head_ok, const BrAcc& acc, float l_tot) {
+  int e[2];
+  slice_exps(acc.O, e);
+  if (!head_ok) return;
+  const int64_t row = (pslot * NB + j) * a.h + n;
+  store_slice_f16(static_cast<_Float16*>(a.part_o) + row * 128, a.part_e + row * 2, acc.O, hh, e);
   if (hh == 0) {
-    float* ml = a.part_ml + ((pslot * NB + j) * a.h + n) * 2;
+    float* ml = a.part_ml + row * 2;
     ml[0] = acc.m;
     ml[1] = l_tot;
   }
@@ -851,7 +909,7 @@ __device__ __forceinline__ void br_run_split(const DecodeArgs& a, const Lens& le
   const int64_t slot0 = int64_t(g) + b;
   const float l0 = halves_sum(first.l);
   if (walk.cur >= walk.end) {
-    if (head_ok) br_store_partial<NB>(a, slot0, j, n, hh, first, l0);
+    br_store_partial<NB>(a, slot0, j, n, hh, head_ok, first, l0);
     return;
   }
   while (next_segment(lens, walk, b, ta, te, L)) {
@@ -865,14 +923,12 @@ __device__ __forceinline__ void br_run_split(const DecodeArgs& a, const Lens& le
                __builtin_amdgcn_readfirstlane(te), j, lane, head_ok, ring, full, cur);
     const float l_tot = halves_sum(cur.l);
     const bool last = walk.cur >= walk.end;
-    if (head_ok) {
-      if (last) br_store_partial<NB>(a, slot0, j, n, hh, first, l0);
-      br_store_partial<NB>(a, int64_t(g) + b, j, n, hh, cur, l_tot);
-    }
+    if (last) br_store_partial<NB>(a, slot0, j, n, hh, head_ok, first, l0);
+    br_store_partial<NB>(a, int64_t(g) + b, j, n, hh, head_ok, cur, l_tot);
     if (last) return;
   }
   // Reached only if the walk ended on a segment short of the split's end.
-  if (head_ok) br_store_partial<NB>(a, slot0, j, n, hh, first, l0);
+  br_store_partial<NB>(a, slot0, j, n, hh, head_ok, first, l0);
 }
 
 // Launch bounds allow one wave per SIMD (the LDS ring admits no more). Built with the MFMA
@@ -1121,14 +1177,38 @@ void decode_hs_kernel(DecodeArgs a) {
     const int64_t pslot = int64_t(gsplit) + b;
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
-    if (head_ok) {
-      float* dst = a.part_o + ((pslot * NB + j) * a.h + head) * DL + (NB == 1 ? 256 * cp : 0);
+    // One exponent per 64-channel block blk of the wave's 256: its channels sit in the four lane
+    // groups g (lanes 16 apart), so the block's largest magnitude takes two exchanges.
+    int e[4];
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
+    for (int blk = 0; blk < 4; ++blk) {
+      float mx = 0.f;
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(O[4 * blk + qq][r]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      e[blk] = part_exp(mx);
+    }
+    if (head_ok) {
+      const int64_t prow = (pslot * NB + j) * a.h + head;
+      const int c0 = NB == 1 ? 256 * cp : 0;  // the wave's first channel of the latent head
+      _Float16* dst = static_cast<_Float16*>(a.part_o) + prow * DL + c0;
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        float v[16];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          *reinterpret_cast<floatx4*>(dst + 64 * blk + 16 * g + 4 * r) =
-              floatx4{O[4 * blk][r], O[4 * blk + 1][r], O[4 * blk + 2][r], O[4 * blk + 3][r]};
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) v[4 * r + qq] = O[4 * blk + qq][r];  // channel 64*blk + 16*g + 4*r + qq
+        *reinterpret_cast<halfx8*>(dst + 64 * blk + 16 * g) = half8_scaled(v, e[blk]);
+        *reinterpret_cast<halfx8*>(dst + 64 * blk + 16 * g + 8) = half8_scaled(v + 8, e[blk]);
+      }
+      if (g == 0) {
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) a.part_e[prow * (DL / kPartBlock) + c0 / kPartBlock + blk] = e[blk];
+      }
       if (g == 0 && (NB == 2 || cp == 0)) {
         float* ml = a.part_ml + ((pslot * NB + j) * a.h + head) * 2;
         ml[0] = m_run;
@@ -1249,7 +1329,8 @@ extern "C" int mlra_decode_splitkv(const void* q_nope, const void* q_rope, const
   a.rope = static_cast<const unsigned char*>(rope_cache);
   a.block_table = block_table;
   a.seqlens = seqlens;
-  a.part_o = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + lay.part_o_off);
+  a.part_o = static_cast<unsigned char*>(workspace) + lay.part_o_off;
+  a.part_e = reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + lay.part_e_off);
   a.part_ml = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + lay.part_ml_off);
   a.prefix = reinterpret_cast<int64_t*>(static_cast<unsigned char*>(workspace) + lay.prefix_off);
   a.counters = reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + lay.counters_off);

@@ -34,7 +34,8 @@ namespace {
 //              write back and invalidate the XCD's whole L2 instead of these few lines.)
 
 struct CombineArgs {
-  const float* part_o;
+  const void* part_o;   // fp32, or fp16 scaled per 64-channel block (bf16 caches)
+  const int* part_e;    // the block exponents of fp16 partials
   const float* part_ml;
   const int64_t* prefix;
   const float* W_UV;
@@ -55,8 +56,8 @@ struct MergeState {
   floatx4 acc[4];
 };
 
-// Fold one unnormalised partial (max m, sum l, four channel quads o) into st.
-__device__ __forceinline__ void merge_in(MergeState& st, float m, float l, const floatx4 (&o)[4]) {
+// Fold one unnormalised partial (max m, sum l, four channel quads o stored as O * 2^-e) into st.
+__device__ __forceinline__ void merge_in(MergeState& st, float m, float l, const floatx4 (&o)[4], int e = 0) {
   if (m == -INFINITY) return;
   if (m > st.M) {
     const float sc = __builtin_amdgcn_exp2f(st.M - m);  // 0 when st.M is -inf
@@ -67,9 +68,12 @@ __device__ __forceinline__ void merge_in(MergeState& st, float m, float l, const
   }
   const float w = __builtin_amdgcn_exp2f(m - st.M);
   st.den = fmaf(w, l, st.den);
+  const float wo = __builtin_amdgcn_ldexpf(w, e);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) st.acc[u] += w * o[u];
+  for (int u = 0; u < 4; ++u) st.acc[u] += wo * o[u];
 }
+
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
 
 // Workgroup barrier that orders LDS only (the W_UV loads issued first stay in flight).
 __device__ __forceinline__ void comb_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -79,7 +83,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t comb_rsrc(const void* p, int b
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), short(0), bytes, 0x00020000);
 }
 
-template <int NB, int DL>
+template <int NB, int DL, typename P>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   constexpr int kBatch = 4;  // slots loaded together
   constexpr int kSteps = kCombBlock / 2;  // K steps of the 32x32x2 MFMA
@@ -132,6 +136,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   // the head when there is none) and skipped through m = -inf.
   floatx2 ml[kBatch];
   floatx4 o[kBatch][4];
+  int ex[kBatch];
   auto load_batch = [&](int64_t g) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -139,9 +144,18 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       const int64_t slot = gl >= 0 ? min(gg, gl) + b : 0;
       const int64_t row = (slot * NB + j) * a.h + i;
       ml[u] = *reinterpret_cast<const floatx2*>(a.part_ml + row * 2);
+      if constexpr (sizeof(P) == 2) {
+        ex[u] = a.part_e[row * (DL / kPartBlock) + c0 / kPartBlock];
+        const _Float16* po = static_cast<const _Float16*>(a.part_o) + row * DL + c0;
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        o[u][v] = *reinterpret_cast<const floatx4*>(a.part_o + row * DL + c0 + 4 * (cq0 + kCombTPS * v));
+        for (int v = 0; v < 4; ++v)
+          o[u][v] = __builtin_convertvector(*reinterpret_cast<const halfx4*>(po + 4 * (cq0 + kCombTPS * v)), floatx4);
+      } else {
+        ex[u] = 0;
+        const float* po = static_cast<const float*>(a.part_o) + row * DL + c0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) o[u][v] = *reinterpret_cast<const floatx4*>(po + 4 * (cq0 + kCombTPS * v));
+      }
       if (gg > gl) ml[u][0] = -INFINITY;
     }
   };
@@ -158,11 +172,11 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) st.acc[u] = floatx4{};
 #pragma unroll
-  for (int u = 0; u < kBatch; ++u) merge_in(st, ml[u][0], ml[u][1], o[u]);
+  for (int u = 0; u < kBatch; ++u) merge_in(st, ml[u][0], ml[u][1], o[u], ex[u]);
   for (int64_t g = gf + r + kBatch * S; g <= gl; g += kBatch * S) {
     load_batch(g);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) merge_in(st, ml[u][0], ml[u][1], o[u]);
+    for (int u = 0; u < kBatch; ++u) merge_in(st, ml[u][0], ml[u][1], o[u], ex[u]);
   }
   if (S > 1) {
     // Tree over the slot parts in a fixed order: at each level, part r + half hands its state
@@ -287,10 +301,16 @@ int device_cus(int* cus) {
 
 using CombineFn = void (*)(CombineArgs);
 
-CombineFn pick_combine(int nb, int dl) {
-  if (nb == 4) return combine_kernel<4, 128>;
-  if (nb == 2) return combine_kernel<2, 256>;
-  return dl == kShardLatent ? combine_kernel<1, kShardLatent> : combine_kernel<1, 512>;
+// The partials of bf16 caches are fp16 (with block exponents), those of fp32 caches fp32.
+template <typename P>
+CombineFn pick_combine_p(int nb, int dl) {
+  if (nb == 4) return combine_kernel<4, 128, P>;
+  if (nb == 2) return combine_kernel<2, 256, P>;
+  return dl == kShardLatent ? combine_kernel<1, kShardLatent, P> : combine_kernel<1, 512, P>;
+}
+
+CombineFn pick_combine(int dtype, int nb, int dl) {
+  return dtype == MLRA_BF16 ? pick_combine_p<_Float16>(nb, dl) : pick_combine_p<float>(nb, dl);
 }
 
 }  // namespace
@@ -311,7 +331,8 @@ extern "C" int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, fl
     return set_error(MLRA_ERR_ALIGN, "out must be 16-byte and W_UV 4-byte aligned");
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   CombineArgs c;
-  c.part_o = reinterpret_cast<const float*>(ws + lay.part_o_off);
+  c.part_o = ws + lay.part_o_off;
+  c.part_e = reinterpret_cast<const int*>(ws + lay.part_e_off);
   c.part_ml = reinterpret_cast<const float*>(ws + lay.part_ml_off);
   c.prefix = reinterpret_cast<const int64_t*>(ws + lay.prefix_off);
   c.W_UV = W_UV;
@@ -327,7 +348,7 @@ extern "C" int mlra_decode_combine(const int32_t* seqlens, const float* W_UV, fl
   if (rc) return rc;
   c.sub = combine_sub(p->batch, p->num_heads, nblk, cus);
   const dim3 grid(p->num_heads, nblk, (p->batch + c.sub - 1) / c.sub);
-  hipLaunchKernelGGL(pick_combine(p->num_branches, p->d_latent), grid, dim3(256), 0,
+  hipLaunchKernelGGL(pick_combine(p->dtype, p->num_branches, p->d_latent), grid, dim3(256), 0,
                      static_cast<hipStream_t>(stream), c);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "combine kernel launch");

@@ -15,10 +15,10 @@ constexpr int kLatentTotal = 512;         // NB * d_latent of the whole-cache fo
 constexpr int kShardLatent = 128;         // d_latent of the one-latent-head shard form (NB = 1)
 constexpr int kDRope = 64;
 constexpr int kDV = 128;
-#ifndef MLRA_COMBINE_BLOCK
-#define MLRA_COMBINE_BLOCK 64
-#endif
-constexpr int kCombBlock = MLRA_COMBINE_BLOCK;  // latent channels per combine workgroup (64 or 128)
+constexpr int kCombBlock = 64;  // latent channels per combine workgroup
+
+// Channels per block of the partials' per-block scale (bf16 caches): one combine workgroup's block.
+constexpr int kPartBlock = kCombBlock;
 
 // Latent channels per cached token: 512, or 128 for the shard form.
 inline int latent_total(const mlra_decode_params& p) { return p.num_branches * p.d_latent; }
@@ -27,8 +27,11 @@ inline int latent_total(const mlra_decode_params& p) { return p.num_branches * p
 inline bool is_shard(const mlra_decode_params& p) { return p.num_branches == 1 && p.d_latent == kShardLatent; }
 
 // Workspace of one decode call:
-//   part_o  fp32 [slots][NB][h][d_latent]  unnormalised output of one split for one sequence
-//                                          (slot = split + sequence)
+//   part_o  [slots][NB][h][d_latent]       unnormalised output of one split for one sequence
+//                                          (slot = split + sequence): fp32 for fp32 caches; for bf16
+//                                          caches fp16, each 64-channel block scaled by 2^-e
+//   part_e  int32 [slots][NB][h][d_latent/64]  e of each 64-channel block (bf16 caches only): the
+//                                          block's largest magnitude is below 2^(e+15)
 //   part_ml fp32 [slots][NB][h][2]         (running max in log2 units, running sum)
 //   prefix  int64 [B + 3]                  first tile of each sequence, then T (total tiles), T, G
 //   ypart   fp32 [groups][h][NB*d_latent/kCombBlock][32][d_v]  projected channel blocks of up to
@@ -39,6 +42,7 @@ inline bool is_shard(const mlra_decode_params& p) { return p.num_branches == 1 &
 struct WorkspaceLayout {
   int64_t slots = 0;
   size_t part_o_off = 0;
+  size_t part_e_off = 0;
   size_t part_ml_off = 0;
   size_t prefix_off = 0;
   size_t ypart_off = 0;

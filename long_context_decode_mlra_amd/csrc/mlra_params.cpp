@@ -31,10 +31,14 @@ WorkspaceLayout workspace_layout(const mlra_decode_params& p, int32_t num_splits
   WorkspaceLayout w;
   // Split g writes at most one partial per sequence it touches, at slot g + b; g + b < G + B.
   w.slots = int64_t(num_splits) + int64_t(p.batch);
-  const size_t per_slot_o = size_t(p.num_heads) * latent_total(p) * sizeof(float);
+  // bf16 caches keep fp16 partials with one int32 exponent per 64-channel block; fp32 caches fp32.
+  const bool half = p.dtype == MLRA_BF16;
+  const size_t per_slot_o = size_t(p.num_heads) * latent_total(p) * (half ? 2 : sizeof(float));
+  const size_t per_slot_e = half ? size_t(p.num_heads) * (latent_total(p) / kPartBlock) * sizeof(int32_t) : 0;
   const size_t per_slot_ml = size_t(p.num_branches) * size_t(p.num_heads) * 2 * sizeof(float);
   w.part_o_off = 0;
-  w.part_ml_off = align256(size_t(w.slots) * per_slot_o);
+  w.part_e_off = align256(size_t(w.slots) * per_slot_o);
+  w.part_ml_off = align256(w.part_e_off + size_t(w.slots) * per_slot_e);
   w.prefix_off = align256(w.part_ml_off + size_t(w.slots) * per_slot_ml);
   const size_t groups = (size_t(p.batch) + 31) / 32;
   w.ypart_off = align256(w.prefix_off + (size_t(p.batch) + 3) * sizeof(int64_t));

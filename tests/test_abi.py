@@ -102,11 +102,13 @@ def test_shard_workspace_size_with_explicit_splits_needs_no_device():
     n = ctypes.c_size_t(0)
     assert L.lib().mlra_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     slots = 1024 + 32
-    expect = (slots * 32 * 128 * 4          # split partials of the output (one latent head)
+    expect = (slots * 32 * 128 * 2          # split partials of the output (one latent head), fp16
+              + slots * 32 * 2 * 4          # one exponent per 64-channel block of each partial
               + slots * 1 * 32 * 2 * 4      # running max and sum per partial
               + (32 + 3) * 8                # tile prefix per sequence, T, G
-              + 1 * 32 * 2 * 32 * 128 * 4)  # projected 64-channel blocks, one group of 32 sequences
-    assert n.value >= expect and n.value % 256 == 0 and n.value < expect + 5 * 256
+              + 1 * 32 * 2 * 32 * 128 * 4   # projected 64-channel blocks, one group of 32 sequences
+              + 32 * 8 * 4)                 # combine arrival counters
+    assert n.value >= expect and n.value % 256 == 0 and n.value < expect + 6 * 256
 
 
 def test_paged_needs_enough_table_columns():
@@ -125,11 +127,16 @@ def test_workspace_size_with_explicit_splits_needs_no_device():
     n = ctypes.c_size_t(0)
     assert L.lib().mlra_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     slots = 512 + 32
-    expect = (slots * 32 * 512 * 4          # split partials of the output
-              + slots * 4 * 32 * 2 * 4      # running max and sum per partial
-              + (32 + 3) * 8                # tile prefix per sequence, T, G
-              + 1 * 32 * 8 * 32 * 128 * 4)  # projected 64-channel blocks, one group of 32 sequences
-    assert n.value >= expect and n.value % 256 == 0 and n.value < expect + 5 * 256
+    for dtype, esz, exps in ((0, 2, 8 * 4), (1, 4, 0)):  # bf16: fp16 partials + block exponents; fp32
+        p = good_params(num_splits=512, dtype=dtype)
+        assert L.lib().mlra_decode_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+        expect = (slots * 32 * 512 * esz        # split partials of the output
+                  + slots * 32 * exps           # one exponent per 64-channel block (bf16 only)
+                  + slots * 4 * 32 * 2 * 4      # running max and sum per partial
+                  + (32 + 3) * 8                # tile prefix per sequence, T, G
+                  + 1 * 32 * 8 * 32 * 128 * 4   # projected 64-channel blocks, one group of 32 sequences
+                  + 32 * 8 * 4)                 # combine arrival counters
+        assert n.value >= expect and n.value % 256 == 0 and n.value < expect + 6 * 256, dtype
 
 
 def test_decode_argument_errors_before_any_launch():
