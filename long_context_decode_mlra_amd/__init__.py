@@ -179,9 +179,12 @@ class Decoder:
         check(lib().mlra_decode_splitkv(_ptr(qn), _ptr(qr), _ptr(lat), _ptr(rp), _ptr(bt), _ptr(sl),
                                         ctypes.byref(self.p), _ptr(self.workspace), self.ws_bytes, _stream(stream)))
 
-    def capture_graph(self) -> "torch.cuda.CUDAGraph":
-        """Record one full decode step (all kernel launches of mlra_decode) into a HIP graph.
-        Replaying it re-runs the step on the same tensors; it records kernel launches only."""
+    def capture_graph(self, steps: int = 1) -> "torch.cuda.CUDAGraph":
+        """Record `steps` consecutive full decode steps (all kernel launches of mlra_decode) into one
+        HIP graph. Replaying it re-runs them on the same tensors; it records kernel launches only.
+        The runtime's gap between graph launches is then paid once per `steps` steps."""
+        if steps < 1:
+            raise ValueError(f"steps must be >= 1 (got {steps})")
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):  # warm-up launch outside the capture
@@ -189,7 +192,8 @@ class Decoder:
         torch.cuda.current_stream().wait_stream(side)
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            self()
+            for _ in range(steps):
+                self()
         return graph
 
     def combine(self, stream=None) -> torch.Tensor:

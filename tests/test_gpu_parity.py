@@ -377,6 +377,32 @@ def test_graph_replay_matches_eager(cfg):
     assert_parity(eager.cpu().double().numpy(), oracle.decode_inputs(inp), label=f"graph cfg{cfg}")
 
 
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_graph_of_several_steps(cfg):
+    """Eight decode steps recorded in one graph: every replay leaves the eager result (each step
+    clears the combine's arrival counters itself, so back-to-back steps in a graph stay exact)."""
+    mlra = _mlra()
+    w = WORKLOADS[cfg].replace(B=5, lengths=("list", (900, 33, 0, 2048, 64)))
+    inp = make_inputs(w, seed=13)
+    d = inp.to("cuda")
+    dec = mlra.Decoder(d.q_nope, d.q_rope, d.latent, d.rope, seqlens=d.seqlens, W_UV=d.W_UV, sm_scale=w.sm_scale,
+                       out_scale=w.gamma, max_seqlen=inp.max_seqlen, block_table=d.block_table,
+                       page_size=w.page_size)
+    eager = dec().clone()
+    torch.cuda.synchronize()
+    graph = dec.capture_graph(steps=8)
+    for k in range(3):
+        dec.out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dec.out, eager), f"replay {k}"
+        junk = torch.randn(1 << 16, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+    with pytest.raises(ValueError):
+        dec.capture_graph(steps=0)
+    assert_parity(eager.cpu().double().numpy(), oracle.decode_inputs(inp), label=f"graph x8 cfg{cfg}")
+
+
 @pytest.mark.parametrize("cfg", [2, 7, 4])
 def test_combine_reruns_on_the_same_partials(cfg):
     """The combine counts its workgroups per (query head, run of sequences) and the last one of a
